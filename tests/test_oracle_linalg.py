@@ -1,0 +1,121 @@
+"""Pins for the oracle's bf16 rounding, GEMM, SwiGLU and error metric (CPU only)."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import BFP4, BFP8
+
+
+def _exact_bf16(v: float) -> Fraction:
+    """Round a float to 8 significant bits (ties to even) in exact rationals."""
+    f = Fraction(v)
+    if f == 0:
+        return f
+    sign = -1 if f < 0 else 1
+    a = abs(f)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    e = max(e, -126)                        # subnormal range: fixed quantum 2**-133
+    q = Fraction(2) ** (e - 7)
+    t = abs(f) / q
+    lo = math.floor(t)
+    rem = t - lo
+    n = lo + 1 if (rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1)) else lo
+    return sign * n * q
+
+
+def test_bf16_round_known_values():
+    r = oracle.bf16_round(np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8 + 2 ** -30),
+                                    2 ** -133, 1.5 * 2 ** -133, 2.5 * 2 ** -133, 0.0, -0.0]))
+    assert r.tolist()[:4] == [1.0, 1.0, 1 + 2 ** -6, -(1 + 2 ** -7)]
+    assert r.tolist()[4:7] == [2 ** -133, 2 * 2 ** -133, 2 * 2 ** -133]
+    assert np.signbit(r[8]) and r[7] == 0
+
+
+def test_bf16_round_vs_exact_rationals():
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(3000) * np.exp2(rng.integers(-140, 100, 3000))
+    # include exact ties
+    v[:200] = (rng.integers(1, 512, 200) + 0.5) * np.exp2(rng.integers(-20, 20, 200) - 8)
+    r = oracle.bf16_round(v)
+    for a, b in zip(v, r):
+        assert Fraction(float(b)) == _exact_bf16(float(a))
+
+
+def test_bf16_round_matches_input_generator_on_fp32():
+    # the input generator's own fp32 -> bf16 rounding and the oracle's agree on fp32 values
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal(20000).astype(np.float32)
+    a = synth.bf16_values(synth.bf16_bits(x)).astype(np.float64)
+    b = oracle.bf16_round(x.astype(np.float64))
+    assert np.array_equal(a, b)
+
+
+def _tiny_case(rng, fmt, m, n, k):
+    w = (rng.standard_normal((n, k)) * 0.3).astype(np.float32)
+    exp, code = oracle.encode(w, fmt)
+    wd = oracle.decode(exp, code, fmt, n, k)
+    xb = synth.bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    return oracle.bf16_to_f64(xb), wd
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+def test_gemm_tiny_vs_exact_rationals(fmt):
+    rng = np.random.default_rng(21 + fmt)
+    for m, n, k in ((1, 3, 16), (2, 8, 64), (2, 5, 48)):
+        x, w = _tiny_case(rng, fmt, m, n, k)
+        y = oracle.gemm(x, w)
+        nrm = oracle.normaliser(x, w)
+        for i in range(m):
+            for j in range(n):
+                exact = sum(Fraction(float(x[i, t])) * Fraction(float(w[j, t])) for t in range(k))
+                # fp64 summation of exact products: error far below 1e-12 of the abs sum
+                assert abs(Fraction(float(y[i, j])) - exact) <= Fraction(1, 10 ** 12) * Fraction(float(nrm[i, j])) + Fraction(0)
+                absum = sum(abs(Fraction(float(x[i, t])) * Fraction(float(w[j, t]))) for t in range(k))
+                assert abs(Fraction(float(nrm[i, j])) - absum) <= Fraction(1, 10 ** 12) * absum
+
+
+def test_gemm_one_hot_is_exact():
+    rng = np.random.default_rng(4)
+    n, k = 16, 128
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    exp, code = oracle.encode(w, BFP8)
+    wd = oracle.decode(exp, code, BFP8, n, k)
+    x = np.zeros((1, k))
+    x[0, 37] = -1.625
+    y = oracle.gemm(x, wd)
+    assert np.array_equal(y[0], -1.625 * wd[:, 37])
+
+
+def test_gemm_orientation():
+    # y[m][n] = sum_k x[m][k] w[n][k]; a transposed operand would fail on this shape
+    x = np.array([[1.0, 2.0, 3.0]])
+    w = np.array([[1.0, 0.0, 0.0], [0.0, 0.0, 1.0]])
+    assert oracle.gemm(x, w).tolist() == [[1.0, 3.0]]
+
+
+def test_silu_and_swiglu():
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    g = np.array([50.0, 700.0, -700.0, -3.0, 0.7, 2.0])
+    s = oracle.silu(g)
+    assert abs(s[0] - 50.0) < 1e-15 * 50
+    assert s[1] == 700.0 and s[2] < 0 and abs(s[2] - (-700.0 * math.exp(-700.0))) <= 1e-15 * abs(s[2])
+    for gv, sv in zip(g[3:], s[3:]):
+        assert abs(sv - gv / (1.0 + math.exp(-gv))) <= 1e-15 * abs(gv)
+    u = np.array([2.0, -1.0, 0.5, 1.0, 1.0, 3.0])
+    assert np.allclose(oracle.swiglu(g, u), s * u, rtol=0, atol=0)
+    assert oracle.linalg.sigmoid(np.array([0.0]))[0] == 0.5
+
+
+def test_rel_err_zero_normaliser():
+    r = oracle.rel_err(np.array([0.0, 1.0, 2.0]), np.array([0.0, 0.5, 2.0]), np.array([0.0, 0.0, 4.0]))
+    assert r[0] == 0.0 and math.isinf(r[1]) and r[2] == 0.0
