@@ -1,0 +1,273 @@
+"""Python binding of libbfp: BFP4/BFP8 weight-streaming matmuls for AMD MI355X (gfx950).
+
+A thin ctypes layer over the C ABI declared in ``include/libbfp.h``. It only marshals
+arguments: every step of the computation runs in the HIP kernels of ``libbfp.so``. PyTorch
+provides device memory and streams. There is no CPU fallback: if ``libbfp.so`` is missing or
+fails to load, every call raises.
+
+Functions keep the C names (``bfp_quantize``, ``bfp_dequantize``, ``bfp_gemm``,
+``bfp_moe_route``, ``bfp_moe_dispatch``, ``bfp_moe_workspace_bytes``, ``bfp_moe_forward``)
+and take torch tensors where the C call takes device pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "BFP4", "BFP8", "BfpError", "BfpMatrix", "MoeLayer", "lib", "library_path",
+    "bfp_quantize", "bfp_dequantize", "bfp_gemm", "bfp_moe_route", "bfp_moe_dispatch",
+    "bfp_moe_workspace_bytes", "bfp_moe_forward", "exp_bytes", "code_bytes",
+]
+
+BFP4 = 4
+BFP8 = 8
+DT_F32 = 0
+DT_BF16 = 1
+EPI_NONE = 0
+EPI_SWIGLU = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libbfp.so")
+
+
+class BfpError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {text} (status {status})")
+        self.status = status
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("exp", ctypes.c_void_p), ("code", ctypes.c_void_p)]
+
+
+class _MoeLayer(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("hidden", ctypes.c_int64), ("inter", ctypes.c_int64),
+                ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("gate", _Tensor), ("up", _Tensor), ("down", _Tensor),
+                ("sh_gate", _Tensor), ("sh_up", _Tensor), ("sh_down", _Tensor),
+                ("sh_gate_w", ctypes.c_void_p)]
+
+
+_LIB = None
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "bfp_version": (ctypes.c_int32, []),
+    "bfp_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
+    "bfp_exp_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+    "bfp_code_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]),
+    "bfp_quantize": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "bfp_dequantize": (ctypes.c_int32, [ctypes.POINTER(_Tensor), ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
+    "bfp_gemm": (ctypes.c_int32, [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
+    "bfp_moe_route": (ctypes.c_int32, [ctypes.POINTER(_MoeLayer), ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "bfp_moe_dispatch": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "bfp_moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_MoeLayer), ctypes.c_int64]),
+    "bfp_moe_forward": (ctypes.c_int32, [ctypes.POINTER(_MoeLayer), ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbfp.so (once). Raises if it is missing: there is no fallback path."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"libbfp.so not built ({path}); run `python -m block_float_quantized_amd.build`")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise BfpError(fn, status, lib().bfp_status_str(status).decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    return t.data_ptr()
+
+
+def exp_bytes(n: int, k: int) -> int:
+    return int(lib().bfp_exp_bytes(n, k))
+
+
+def code_bytes(fmt: int, n: int, k: int) -> int:
+    return int(lib().bfp_code_bytes(fmt, n, k))
+
+
+@dataclass
+class BfpMatrix:
+    """A BFP matrix in device memory: exponent plane [n][k/16] and code plane (uint8)."""
+    fmt: int
+    n: int
+    k: int
+    exp: torch.Tensor
+    code: torch.Tensor
+
+    def view(self) -> _Tensor:
+        return _Tensor(self.fmt, self.n, self.k, _ptr(self.exp), _ptr(self.code))
+
+    def rows(self, r0: int, r1: int) -> "BfpMatrix":
+        """Rows [r0, r1) as a view (no copy)."""
+        nb = self.k // 16
+        cpr = self.code.numel() // self.n
+        return BfpMatrix(self.fmt, r1 - r0, self.k, self.exp.view(-1)[r0 * nb:r1 * nb],
+                         self.code.view(-1)[r0 * cpr:r1 * cpr])
+
+    @property
+    def nbytes(self) -> int:
+        return self.exp.numel() + self.code.numel()
+
+
+def empty_matrix(fmt: int, n: int, k: int, device="cuda") -> BfpMatrix:
+    exp = torch.empty(exp_bytes(n, k), dtype=torch.uint8, device=device)
+    code = torch.empty(code_bytes(fmt, n, k), dtype=torch.uint8, device=device)
+    return BfpMatrix(fmt, n, k, exp, code)
+
+
+def bfp_quantize(fmt: int, w: torch.Tensor, out: BfpMatrix | None = None, stream=None) -> BfpMatrix:
+    """Encode a device fp32 [n][k] matrix (synchronizes the stream)."""
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous fp32 [n][k] device tensor")
+    n, k = w.shape
+    if out is None:
+        out = empty_matrix(fmt, n, k, w.device)
+    _check("bfp_quantize", lib().bfp_quantize(fmt, _ptr(w), n, k, _ptr(out.exp), _ptr(out.code), _stream(stream)))
+    return out
+
+
+def bfp_dequantize(w: BfpMatrix, dtype=torch.float32, stream=None) -> torch.Tensor:
+    dt = DT_BF16 if dtype == torch.bfloat16 else DT_F32
+    out = torch.empty((w.n, w.k), dtype=dtype, device=w.exp.device)
+    v = w.view()
+    _check("bfp_dequantize", lib().bfp_dequantize(ctypes.byref(v), dt, _ptr(out), _stream(stream)))
+    return out
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    if t.dtype == torch.float32:
+        return DT_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def bfp_gemm(w: BfpMatrix, x: torch.Tensor, w_up: BfpMatrix | None = None, out_dtype=torch.float32,
+             out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = x W^T (or silu(x W^T) * (x Wup^T) when w_up is given); x is [m][k], m <= 32."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a row-major [m][k] device tensor")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
+    vw = w.view()
+    vu = w_up.view() if w_up is not None else None
+    st = lib().bfp_gemm(ctypes.byref(vw), ctypes.byref(vu) if vu is not None else None,
+                        EPI_SWIGLU if w_up is not None else EPI_NONE,
+                        _ptr(x), _dt(x), m, x.stride(0), _ptr(out), _dt(out), out.stride(0), _stream(stream))
+    _check("bfp_gemm", st)
+    return out
+
+
+@dataclass
+class MoeLayer:
+    """Device tensors of one MoE layer (see bfp_moe_layer in include/libbfp.h)."""
+    n_experts: int
+    top_k: int
+    hidden: int
+    inter: int
+    router_w: torch.Tensor            # bf16 bits as int16/uint16 or bfloat16 [E][hidden]
+    router_bias: torch.Tensor | None  # fp32 [E]
+    gate: BfpMatrix
+    up: BfpMatrix
+    down: BfpMatrix
+    sh_gate: BfpMatrix | None
+    sh_up: BfpMatrix | None
+    sh_down: BfpMatrix | None
+    sh_gate_w: torch.Tensor | None    # bf16 [hidden]
+
+    def view(self) -> _MoeLayer:
+        absent = _Tensor(0, 0, 0, None, None)
+        return _MoeLayer(self.n_experts, self.top_k, self.hidden, self.inter,
+                         _ptr(self.router_w), _ptr(self.router_bias),
+                         self.gate.view(), self.up.view(), self.down.view(),
+                         self.sh_gate.view() if self.sh_gate is not None else absent,
+                         self.sh_up.view() if self.sh_up is not None else absent,
+                         self.sh_down.view() if self.sh_down is not None else absent,
+                         _ptr(self.sh_gate_w))
+
+
+def bfp_moe_route(layer: MoeLayer, x: torch.Tensor, stream=None):
+    """Routing step: returns (ids int32 [m][top_k], weights fp32 [m][top_k], g fp32 [m])."""
+    m = x.shape[0]
+    ids = torch.empty((m, layer.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((m, layer.top_k), dtype=torch.float32, device=x.device)
+    g = torch.empty((m,), dtype=torch.float32, device=x.device)
+    v = layer.view()
+    _check("bfp_moe_route", lib().bfp_moe_route(ctypes.byref(v), _ptr(x), m, _ptr(ids), _ptr(w), _ptr(g),
+                                                _stream(stream)))
+    return ids, w, g
+
+
+def bfp_moe_dispatch(ids: torch.Tensor, n_experts: int, stream=None):
+    """Counting sort by expert: returns (counts [E], offsets [E+1], perm [m*top_k]) int32."""
+    m, top_k = ids.shape
+    counts = torch.empty((n_experts,), dtype=torch.int32, device=ids.device)
+    offsets = torch.empty((n_experts + 1,), dtype=torch.int32, device=ids.device)
+    perm = torch.empty((m * top_k,), dtype=torch.int32, device=ids.device)
+    _check("bfp_moe_dispatch", lib().bfp_moe_dispatch(_ptr(ids), m, top_k, n_experts, _ptr(counts),
+                                                      _ptr(offsets), _ptr(perm), _stream(stream)))
+    return counts, offsets, perm
+
+
+def bfp_moe_workspace_bytes(layer: MoeLayer, m: int) -> int:
+    v = layer.view()
+    return int(lib().bfp_moe_workspace_bytes(ctypes.byref(v), m))
+
+
+def bfp_moe_forward(layer: MoeLayer, x: torch.Tensor, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, topk_ids: torch.Tensor | None = None,
+                    topk_w: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = MoE(x) for x bf16 [m][hidden]; returns fp32 [m][hidden]."""
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, layer.hidden), dtype=torch.float32, device=x.device)
+    need = bfp_moe_workspace_bytes(layer, m)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
+    v = layer.view()
+    st = lib().bfp_moe_forward(ctypes.byref(v), _ptr(x), m, _ptr(out), _ptr(topk_ids), _ptr(topk_w),
+                               _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("bfp_moe_forward", st)
+    return out

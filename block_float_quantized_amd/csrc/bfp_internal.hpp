@@ -1,0 +1,37 @@
+// Internal interface between the C ABI (api.cpp) and the kernel launchers (*.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bfp {
+
+// Encode fp32 [n][k] into exponent and code planes; `flag` is a device int set to 1 when a
+// non-finite value is met (the caller clears it before and reads it after).
+hipError_t quantize_launch(int fmt, const float* w, int64_t n, int64_t k, uint8_t* exp,
+                           uint8_t* code, int* flag, hipStream_t s);
+
+// Decode a whole matrix to fp32 or bf16 [n][k].
+hipError_t dequant_launch(int fmt, const uint8_t* exp, const uint8_t* code, int64_t n, int64_t k,
+                          int out_bf16, void* out, hipStream_t s);
+
+struct GemvParams {
+  int fmt;
+  const uint8_t* w_exp;
+  const uint8_t* w_code;
+  const uint8_t* u_exp;        // SwiGLU up-projection, or null
+  const uint8_t* u_code;
+  int64_t n, k;
+  const void* x;
+  int64_t ldx;
+  int x_bf16;
+  int64_t m;
+  void* y;
+  int64_t ldy;
+  int y_bf16;
+};
+
+hipError_t gemv_launch(const GemvParams& g, hipStream_t s);
+
+}  // namespace bfp

@@ -1,0 +1,194 @@
+/*
+ * libbfp — block-floating-point (BFP4 / BFP8) weight-streaming matmuls for AMD MI355X (gfx950).
+ *
+ * The operations follow the model-card pages on the TT-native mixed BFP4/BFP8 Qwen
+ * checkpoints:
+ *  - "Qwen3.8-27B — TT-native mixed BFP4/BFP8 (GPTQ), single P150" (revision
+ *    gptq-ctx2-20261002, "What changed in this release", GPTQ bullet): BFP4 matrices are
+ *    made of 16-value blocks; values already representable re-encode bit for bit.
+ *  - "Qwen3.6-35B-A3B — TT-native mixed BFP4/BFP8 (GPTQ experts), single P150"
+ *    ("What is in this release", "Precision as served", "Fused decode kernels",
+ *    "Verification"): routed and shared experts in BFP4, dense projections and the LM
+ *    head in BFP8 (round to nearest), BF16 router, device top-k routing, BFP tensors
+ *    converted bit-exactly by round to nearest.
+ *  - "qwen3.6-a3b-blackhole" bundle page, introduction: a 256-expert top-8 MoE plus a
+ *    shared expert in every layer.
+ *  - "Qwen3.8-27B ..." ("What changed in this release (s27v6-20261024)", "Multi-user
+ *    decode"): up to 32 rows share one pass over every weight; prefill in 2,048-token
+ *    chunks.
+ *
+ * Format. A matrix W is stored [N][K] (N output rows, reduction along K, K a multiple of
+ * 16) as two planes, row-major in block order:
+ *   exp  : uint8 [N][K/16]   shared exponent E of each 16-value block
+ *   code : BFP8 uint8 [N][K]   one byte per value, sign<<7 | magnitude (7 bits)
+ *          BFP4 uint8 [N][K/2] value 2j in the low nibble of byte j, 2j+1 in the high
+ *                              nibble, each nibble sign<<3 | magnitude (3 bits)
+ * Value i of a block decodes to (-1)^sign_i * mag_i * 2^(E - 127 - (m - 1)), m = 7 or 3.
+ * Encoding: E = the largest fp32 exponent field in the block; mag = |v| * 2^-(E-127-(m-1))
+ * rounded to nearest, ties to even, clamped to 2^m - 1; the sign bit is copied (so -0.0
+ * and values that round to 0 keep their sign). Inf/NaN are rejected.
+ *
+ * Conventions for every call:
+ *  - Pointers named "device" are device memory owned by the caller; the library keeps no
+ *    reference to them after the call returns. Host-side structs are read during the call.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls are stream-ordered and
+ *    asynchronous except bfp_quantize, which synchronizes `stream` to report non-finite
+ *    input.
+ *  - Errors are returned as bfp_status codes; argument checks happen on the host before
+ *    any launch, so an error means nothing was launched. No call aborts or throws.
+ *  - Device pointers must be 16-byte aligned; leading dimensions are in elements.
+ *  - Calls on different streams may run concurrently; calls that write the same output
+ *    or workspace on different streams race.
+ */
+#ifndef LIBBFP_H
+#define LIBBFP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BFP_OK = 0,
+  BFP_E_ARG = 1,          /* null pointer, unknown enum value, inconsistent struct */
+  BFP_E_SHAPE = 2,        /* k not a multiple of 16, m or n out of range, mismatched shapes */
+  BFP_E_ALIGN = 3,        /* a device pointer is not 16-byte aligned */
+  BFP_E_NONFINITE = 4,    /* bfp_quantize met Inf or NaN (outputs are then unspecified) */
+  BFP_E_WORKSPACE = 5,    /* workspace missing or smaller than bfp_moe_workspace_bytes */
+  BFP_E_DEVICE = 6,       /* a HIP runtime call or kernel launch failed */
+  BFP_E_UNSUPPORTED = 7   /* a valid request this build does not implement */
+} bfp_status;
+
+enum { BFP_FMT_BFP4 = 4, BFP_FMT_BFP8 = 8 };
+enum { BFP_DT_F32 = 0, BFP_DT_BF16 = 1 };
+enum { BFP_EPI_NONE = 0, BFP_EPI_SWIGLU = 1 };
+
+/* Non-owning view of one BFP matrix in device memory (layout above). */
+typedef struct bfp_tensor {
+  int32_t fmt;            /* BFP_FMT_BFP4 or BFP_FMT_BFP8; 0 marks an absent tensor */
+  int64_t n;              /* rows (outputs) */
+  int64_t k;              /* values per row, a multiple of 16 */
+  const uint8_t *exp;     /* device, [n][k/16] */
+  const uint8_t *code;    /* device, [n][k] (BFP8) or [n][k/2] (BFP4) */
+} bfp_tensor;
+
+/* Largest number of activation rows one bfp_gemm call streams the weights for. */
+#define BFP_GEMM_MAX_M 32
+/* Largest number of tokens one bfp_moe_forward call takes. */
+#define BFP_MOE_MAX_M 8192
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t bfp_version(void);
+
+/* Human-readable name of a status code (a static string; never NULL). */
+const char *bfp_status_str(int32_t status);
+
+/* Bytes of the exponent plane of an n x k matrix: n * k / 16. */
+size_t bfp_exp_bytes(int64_t n, int64_t k);
+
+/* Bytes of the code plane: n * k (BFP8) or n * k / 2 (BFP4); 0 for an unknown format. */
+size_t bfp_code_bytes(int32_t fmt, int64_t n, int64_t k);
+
+/*
+ * Encode (round to nearest, ties to even; see Format). w: device fp32 [n][k], row stride k.
+ * exp, code: device outputs sized by bfp_exp_bytes / bfp_code_bytes. Bit-exact: the same
+ * input gives the same bytes on every run and device ("Qwen3.6-35B-A3B ...",
+ * "Verification": the round-to-nearest conversion is bit-exact). Synchronizes `stream`;
+ * returns BFP_E_NONFINITE if any input value is Inf or NaN.
+ */
+int32_t bfp_quantize(int32_t fmt, const float *w, int64_t n, int64_t k,
+                     uint8_t *exp, uint8_t *code, void *stream);
+
+/*
+ * Decode a whole matrix: out[n][k] = (-1)^sign * mag * 2^s, exact, in fp32
+ * (out_dtype = BFP_DT_F32) or bf16 (BFP_DT_BF16; every BFP value is bf16-representable).
+ */
+int32_t bfp_dequantize(const bfp_tensor *w, int32_t out_dtype, void *out, void *stream);
+
+/*
+ * Skinny matmul over streamed BFP weights, dequantized in registers:
+ *   epilogue NONE  : y[i][j] = sum_k x[i][k] * W[j][k]
+ *   epilogue SWIGLU: y[i][j] = silu(sum_k x[i][k] * W[j][k]) * (sum_k x[i][k] * Wup[j][k])
+ * with silu(g) = g / (1 + e^-g). i < m (1..BFP_GEMM_MAX_M rows share one pass over the
+ * weights), j < w->n, k < w->k. x: device [m][ldx] of x_dtype (bf16 or fp32); y: device
+ * [m][ldy] of y_dtype (fp32, or bf16 rounded to nearest even). Products are exact and
+ * sums are fp32. w_up must be NULL for NONE and match w's format and shape for SWIGLU.
+ */
+int32_t bfp_gemm(const bfp_tensor *w, const bfp_tensor *w_up, int32_t epilogue,
+                 const void *x, int32_t x_dtype, int64_t m, int64_t ldx,
+                 void *y, int32_t y_dtype, int64_t ldy, void *stream);
+
+/*
+ * One MoE layer with BFP4 experts ("qwen3.6-a3b-blackhole", introduction; "Qwen3.6-35B-A3B
+ * ...", "Precision as served" and "Fused decode kernels").
+ * Routed experts are stacked along the rows: gate and up have n = n_experts * inter,
+ * k = hidden (expert e owns rows [e*inter, (e+1)*inter)); down has n = n_experts * hidden,
+ * k = inter. The shared expert has the same shapes for a single expert; set sh_gate.fmt = 0
+ * for none. router_w: device bf16 [n_experts][hidden]; router_bias: device fp32
+ * [n_experts] or NULL; sh_gate_w: device bf16 [hidden] (shared-expert sigmoid gate) or
+ * NULL for a gate of 1.
+ */
+typedef struct bfp_moe_layer {
+  int32_t n_experts;      /* routed experts, 1..256 */
+  int32_t top_k;          /* experts per token, 1..8 */
+  int64_t hidden;         /* model width (multiple of 16) */
+  int64_t inter;          /* expert width (multiple of 16) */
+  const uint16_t *router_w;
+  const float *router_bias;
+  bfp_tensor gate, up, down;
+  bfp_tensor sh_gate, sh_up, sh_down;
+  const uint16_t *sh_gate_w;
+} bfp_moe_layer;
+
+/*
+ * Routing step of bfp_moe_forward, exposed on its own. For each token t < m:
+ *   l_e = sum_k x[t][k] * router_w[e][k] (+ router_bias[e]), exact bf16 products summed
+ *         in fp64;
+ *   ids[t][0..top_k) = the top_k experts by (l descending, e ascending), in that order;
+ *   w[t][j] = softmax over all experts restricted to the selection and renormalised
+ *             (= exp(l_ej - l_max) / sum over the selection), fp32;
+ *   g[t] = sigmoid(x[t] . sh_gate_w) (1 if sh_gate_w is NULL), fp32.
+ * x: device bf16 [m][hidden]; ids: device int32 [m][top_k]; w: device fp32 [m][top_k];
+ * g: device fp32 [m] or NULL.
+ */
+int32_t bfp_moe_route(const bfp_moe_layer *L, const uint16_t *x, int64_t m,
+                      int32_t *ids, float *w, float *g, void *stream);
+
+/*
+ * Dispatch structure for expert-grouped execution (counting sort by expert):
+ *   counts[e]  = number of (token, slot) pairs routed to expert e;
+ *   offsets[e] = sum of counts below e (n_experts + 1 entries, offsets[n_experts] = m*top_k);
+ *   perm[p]    = pair ids top_k*t + j ordered by (expert ascending, token ascending).
+ * ids: device int32 [m][top_k], every entry in [0, n_experts) and distinct within a row.
+ * counts: device int32 [n_experts]; offsets: device int32 [n_experts + 1];
+ * perm: device int32 [m * top_k]. Bit-exact (integer work).
+ */
+int32_t bfp_moe_dispatch(const int32_t *ids, int64_t m, int32_t top_k, int32_t n_experts,
+                         int32_t *counts, int32_t *offsets, int32_t *perm, void *stream);
+
+/* Workspace bytes bfp_moe_forward needs for m tokens (0 if the layer or m is invalid). */
+size_t bfp_moe_workspace_bytes(const bfp_moe_layer *L, int64_t m);
+
+/*
+ * Full MoE layer: y[t] = sum_j w[t][j] * Down_ej(silu(Gate_ej x_t) * Up_ej x_t)
+ *                        + g[t] * Shared(x_t),
+ * routing as in bfp_moe_route. Every selected expert's weights are streamed once per call
+ * for all tokens that chose it. m <= 32 runs the skinny decode path (h = silu(gate)*up kept
+ * in fp32); larger m runs the prefill path, where tokens are grouped by expert and h is
+ * rounded to bf16 (nearest even) before the down projection, which is then a bf16
+ * matrix-core product with fp32 accumulation.
+ * x: device bf16 [m][hidden]; y: device fp32 [m][hidden]; topk_ids / topk_w: optional
+ * device outputs [m][top_k] (NULL to skip); ws: device workspace of at least
+ * bfp_moe_workspace_bytes(L, m) bytes (contents on return unspecified).
+ */
+int32_t bfp_moe_forward(const bfp_moe_layer *L, const uint16_t *x, int64_t m, float *y,
+                        int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
+                        void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBBFP_H */

@@ -1,0 +1,81 @@
+"""The C-ABI library loads, exports every function include/libbfp.h declares, and rejects
+bad arguments on the host before touching a device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_float_quantized_amd as bfq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "libbfp.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(bfp_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert "bfp_gemm" in names and "bfp_quantize" in names and "bfp_moe_forward" in names
+    handle = ctypes.CDLL(bfq.library_path())
+    for name in names:
+        assert hasattr(handle, name), name
+    # the binding knows every declared function
+    assert set(names) <= set(bfq._SIGS)
+
+
+def test_status_strings_and_sizes():
+    lib = bfq.lib()
+    assert lib.bfp_status_str(0) == b"ok"
+    assert lib.bfp_status_str(4).startswith(b"non-finite")
+    assert lib.bfp_status_str(99) == b"unknown status"
+    assert lib.bfp_exp_bytes(5120, 17408) == 5120 * 1088
+    assert lib.bfp_code_bytes(4, 5120, 17408) == 5120 * 8704
+    assert lib.bfp_code_bytes(8, 2048, 2048) == 2048 * 2048
+    assert lib.bfp_code_bytes(5, 16, 16) == 0
+
+
+def _tensor(fmt=4, n=32, k=64, exp=16, code=16):
+    return bfq._Tensor(fmt, n, k, exp, code)
+
+
+def test_host_validation_before_any_launch():
+    lib = bfq.lib()
+    # quantize
+    assert lib.bfp_quantize(5, 16, 4, 16, 16, 16, None) == 1          # unknown format
+    assert lib.bfp_quantize(4, None, 4, 16, 16, 16, None) == 1         # null pointer
+    assert lib.bfp_quantize(4, 16, 4, 24, 16, 16, None) == 2           # k % 16
+    assert lib.bfp_quantize(4, 16, 0, 16, 16, 16, None) == 2           # n = 0
+    assert lib.bfp_quantize(4, 18, 4, 16, 16, 16, None) == 3           # misaligned input
+    # dequantize
+    t = _tensor(k=40)
+    assert lib.bfp_dequantize(ctypes.byref(t), 0, 16, None) == 2
+    t = _tensor(code=24)
+    assert lib.bfp_dequantize(ctypes.byref(t), 0, 16, None) == 3
+    t = _tensor()
+    assert lib.bfp_dequantize(ctypes.byref(t), 7, 16, None) == 1
+    # gemm
+    w = _tensor()
+    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 0, 64, 16, 0, 32, None) == 2     # m = 0
+    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 33, 64, 16, 0, 32, None) == 2    # m > 32
+    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 1, 32, 16, 0, 32, None) == 2     # ldx < k
+    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 1, 68, 16, 0, 32, None) == 3     # ldx*2 % 16
+    assert lib.bfp_gemm(ctypes.byref(w), None, 1, 16, 1, 1, 64, 16, 0, 32, None) != 0     # SwiGLU without up
+    u = _tensor(n=16)
+    assert lib.bfp_gemm(ctypes.byref(w), ctypes.byref(u), 1, 16, 1, 1, 64, 16, 0, 32, None) == 2
+    u = _tensor(fmt=8)
+    assert lib.bfp_gemm(ctypes.byref(w), ctypes.byref(u), 1, 16, 1, 1, 64, 16, 0, 32, None) == 1
+    assert lib.bfp_gemm(ctypes.byref(w), ctypes.byref(w), 0, 16, 1, 1, 64, 16, 0, 32, None) == 1
+    assert lib.bfp_gemm(ctypes.byref(w), None, 3, 16, 1, 1, 64, 16, 0, 32, None) == 1
+
+
+def test_python_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(bfq, "_LIB", None)
+    monkeypatch.setattr(bfq, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        bfq.lib()

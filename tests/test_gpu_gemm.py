@@ -1,0 +1,181 @@
+"""GPU skinny BFP matmul (bfp_gemm) against the oracle.
+
+Tolerance: every fp32 output within 2e-3 of sum_k |x_k w_k| (computed by the oracle in
+fp64). bf16 outputs additionally get half a bf16 ulp of the exact value for their final
+rounding. One-hot activations must match bit for bit (one exact product, no sums).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_float_quantized_amd as bfq
+import oracle
+import synth
+from oracle import BFP4, BFP8
+from gpu_util import assert_within, dev_bf16, dev_f32, host_bits_bf16, matrix_from_oracle, note
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _case(fmt, n, k, m, seed, x_dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * 0.02 * rng.lognormal(0, 0.5, (n, 1))).astype(np.float32)
+    exp, code = oracle.encode(w, fmt)
+    wd = oracle.decode(exp, code, fmt, n, k)
+    if x_dtype == "bf16":
+        xb = synth.bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+        x64 = oracle.bf16_to_f64(xb)
+        xt = dev_bf16(xb)
+    else:
+        xf = rng.standard_normal((m, k)).astype(np.float32)
+        x64 = xf.astype(np.float64)
+        xt = dev_f32(xf)
+    return matrix_from_oracle(fmt, exp, code, n, k), wd, x64, xt
+
+
+def _bf16_values(bits):
+    return synth.bf16_values(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+@pytest.mark.parametrize("n,k", [(1, 16), (37, 48), (129, 1040), (300, 2064), (70, 512)])
+@pytest.mark.parametrize("m", [1, 3, 8, 13, 32])
+def test_gemm_small_shapes(fmt, n, k, m):
+    note(f"gemm fmt={fmt} n={n} k={k} m={m}")
+    wm, wd, x64, xt = _case(fmt, n, k, m, seed=n * 7 + k + m + fmt)
+    y = bfq.bfp_gemm(wm, xt).cpu().numpy()
+    assert_within(y, oracle.gemm(x64, wd), oracle.normaliser(x64, wd), TOL, what="gemm")
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+@pytest.mark.parametrize("m", [1, 5, 16])
+def test_gemm_fp32_x_and_bf16_y(fmt, m):
+    note(f"gemm fp32-x bf16-y fmt={fmt} m={m}")
+    wm, wd, x64, xt = _case(fmt, 203, 3088, m, seed=m + 100 * fmt, x_dtype="f32")
+    y = bfq.bfp_gemm(wm, xt, out_dtype=torch.bfloat16)
+    yv = _bf16_values(host_bits_bf16(y))
+    ref = oracle.gemm(x64, wd)
+    assert_within(yv, ref, oracle.normaliser(x64, wd), TOL, extra=2.0 ** -8 * np.abs(ref), what="gemm bf16 out")
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+@pytest.mark.parametrize("m", [1, 4, 32])
+def test_gemm_swiglu(fmt, m):
+    note(f"gemm swiglu fmt={fmt} m={m}")
+    n, k = 333, 2080
+    wg, gd, x64, xt = _case(fmt, n, k, m, seed=m + 11 * fmt)
+    rng = np.random.default_rng(m + 5)
+    wu = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    eu, cu = oracle.encode(wu, fmt)
+    ud = oracle.decode(eu, cu, fmt, n, k)
+    um = matrix_from_oracle(fmt, eu, cu, n, k)
+    h = bfq.bfp_gemm(wg, xt, w_up=um).cpu().numpy()
+    g, u = oracle.gemm(x64, gd), oracle.gemm(x64, ud)
+    ref = oracle.swiglu(g, u)
+    # the tolerance carries through silu: |dh| <= |silu'(g)| |dg| |u| + |silu(g)| |du|
+    ng, nu = oracle.normaliser(x64, gd), oracle.normaliser(x64, ud)
+    norm = 1.1 * ng * np.abs(u) + np.abs(oracle.silu(g)) * nu   # |silu'| < 1.1 everywhere
+    assert_within(h, ref, norm, TOL, extra=1e-6 * np.abs(ref), what="swiglu")
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+def test_gemm_one_hot_bit_exact(fmt):
+    note(f"gemm one-hot fmt={fmt}")
+    n, k = 200, 1056
+    wm, wd, _, _ = _case(fmt, n, k, 1, seed=3 + fmt)
+    xb = np.zeros((2, k), np.uint16)
+    xb[0, 777] = synth.bf16_bits(np.array([-1.375], np.float32))[0]
+    xb[1, 5] = synth.bf16_bits(np.array([3.0e-3], np.float32))[0]
+    y = bfq.bfp_gemm(wm, dev_bf16(xb)).cpu().numpy()
+    want = (oracle.bf16_to_f64(xb) @ wd.T).astype(np.float32)
+    assert np.array_equal(y.view(np.uint32), want.view(np.uint32))
+
+
+def test_gemm_rows_are_independent_of_m():
+    """Row i of an m-row call equals the same row computed alone (same reduction order)."""
+    note("gemm batch invariance")
+    wm, wd, x64, xt = _case(BFP4, 150, 4096, 8, seed=77)
+    y8 = bfq.bfp_gemm(wm, xt).cpu().numpy()
+    y1 = np.stack([bfq.bfp_gemm(wm, xt[i:i + 1].contiguous()).cpu().numpy()[0] for i in range(8)])
+    assert np.array_equal(y8.view(np.uint32), y1.view(np.uint32))
+
+
+def test_gemm_deterministic():
+    note("gemm determinism")
+    wm, wd, x64, xt = _case(BFP8, 999, 2048, 16, seed=5)
+    a = bfq.bfp_gemm(wm, xt)
+    b = bfq.bfp_gemm(wm, xt)
+    assert torch.equal(a, b)
+
+
+# ---- workload sizes ------------------------------------------------------------------------
+
+def _sampled_rows(n, count, seed):
+    return np.unique(np.concatenate([[0, n - 1], np.random.default_rng(seed).integers(0, n, count)]))
+
+
+def test_workload_single_bfp8_gemv():
+    """2048 x 2048 BFP8, x 1 x 2048, all outputs."""
+    note("workload: single BFP8 GEMV 2048x2048")
+    c = synth.gemv_case(0)
+    w = c["w"]
+    m = bfq.bfp_quantize(BFP8, dev_f32(w))
+    exp, code = oracle.encode(w, BFP8)
+    wd = oracle.decode(exp, code, BFP8, *w.shape)
+    x64 = oracle.bf16_to_f64(c["x"])
+    y = bfq.bfp_gemm(m, dev_bf16(c["x"])).cpu().numpy()
+    assert_within(y, oracle.gemm(x64, wd), oracle.normaliser(x64, wd), TOL, what="gemv2048")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 32])
+def test_workload_dense_mlp(M):
+    """27B-class BFP4 MLP: gate/up 5120->17408 with SwiGLU, down 17408->5120, bf16 out.
+    Gate/up checked on sampled rows; down checked on sampled outputs with the GPU's h as
+    its input (each GEMV against the oracle on identical operands)."""
+    note(f"workload: dense BFP4 MLP M={M}")
+    c = synth.mlp_case(M, 0)
+    g = bfq.bfp_quantize(BFP4, dev_f32(c["wg"]))
+    u = bfq.bfp_quantize(BFP4, dev_f32(c["wu"]))
+    d = bfq.bfp_quantize(BFP4, dev_f32(c["wd"]))
+    x = dev_bf16(c["x"])
+    h = bfq.bfp_gemm(g, x, w_up=u)
+    y = bfq.bfp_gemm(d, h, out_dtype=torch.bfloat16)
+    h_np = h.cpu().numpy()
+    y_np = _bf16_values(host_bits_bf16(y))
+    x64 = oracle.bf16_to_f64(c["x"])
+    rows = _sampled_rows(17408, 96, M)
+    eg, cg = oracle.encode(c["wg"][rows], BFP4)
+    eu, cu = oracle.encode(c["wu"][rows], BFP4)
+    gd = oracle.decode(eg, cg, BFP4, len(rows), 5120)
+    ud = oracle.decode(eu, cu, BFP4, len(rows), 5120)
+    gg, uu = oracle.gemm(x64, gd), oracle.gemm(x64, ud)
+    ref = oracle.swiglu(gg, uu)
+    ng, nu = oracle.normaliser(x64, gd), oracle.normaliser(x64, ud)
+    norm = 1.1 * ng * np.abs(uu) + np.abs(oracle.silu(gg)) * nu
+    assert_within(h_np[:, rows], ref, norm, TOL, extra=1e-6 * np.abs(ref), what="mlp h")
+    outs = _sampled_rows(5120, 96, M + 1)
+    ed, cd = oracle.encode(c["wd"][outs], BFP4)
+    dd = oracle.decode(ed, cd, BFP4, len(outs), 17408)
+    h64 = h_np.astype(np.float64)
+    ref = oracle.gemm(h64, dd)
+    assert_within(y_np[:, outs], ref, oracle.normaliser(h64, dd), TOL, extra=2.0 ** -8 * np.abs(ref), what="mlp y")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_workload_bfp8_projections_and_lm_head(M):
+    """Fused QKV 2048->5120, O 4096->2048, LM head 2048->151936 (sampled rows), fp32 out."""
+    note(f"workload: BFP8 projections + LM head M={M}")
+    c = synth.proj_case(M, 0)
+    x64 = oracle.bf16_to_f64(c["x"])
+    xo64 = oracle.bf16_to_f64(c["xo"])
+    for name, xx, x_bits in (("wqkv", x64, c["x"]), ("wo", xo64, c["xo"]), ("wlm", x64, c["x"])):
+        w = c[name]
+        n, k = w.shape
+        m = bfq.bfp_quantize(BFP8, dev_f32(w))
+        y = bfq.bfp_gemm(m, dev_bf16(x_bits)).cpu().numpy()
+        rows = _sampled_rows(n, 256, M + n)
+        e, cc = oracle.encode(w[rows], BFP8)
+        wd = oracle.decode(e, cc, BFP8, len(rows), k)
+        assert_within(y[:, rows], oracle.gemm(xx, wd), oracle.normaliser(xx, wd), TOL, what=name)
+        del m
