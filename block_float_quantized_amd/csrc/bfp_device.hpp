@@ -26,6 +26,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Exponent offset that turns the raw block exponent E into the log2 of the per-block
 // multiplier applied to the unpacked integers (see the file comment).
@@ -68,6 +69,36 @@ __device__ __forceinline__ void unpack4_bfp8(uint32_t c, float w[4]) {
   w[1] = __uint_as_float(__float_as_uint(m1) | ((c << 16) & 0x80000000u));
   w[2] = __uint_as_float(__float_as_uint(m2) | ((c << 8) & 0x80000000u));
   w[3] = __uint_as_float(__float_as_uint(m3) | (c & 0x80000000u));
+}
+
+// Eight BFP4 nibbles -> four dwords of bf16 pairs (-1)^s * mag * 2^-9, in the pair order
+// (v0,v2) (v4,v6) (v1,v3) (v5,v7); activations are staged in the same order.
+__device__ __forceinline__ void unpack8_bfp4_bf16(uint32_t c, uint32_t w[4]) {
+  const uint32_t ev = ((c << 4) & 0x80808080u) | (c & 0x07070707u);
+  const uint32_t od = (c & 0x80808080u) | ((c >> 4) & 0x07070707u);
+  w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, 1.0f, false));
+  w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, 1.0f, true));
+  w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, 1.0f, false));
+  w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, 1.0f, true));
+}
+
+// Four BFP8 codes -> two dwords of bf16 pairs (-1)^s * mag in the order (v0,v2) (v1,v3).
+// Integers up to 127 have at most 7 significant bits, so the top half of the fp32 is the
+// exact bf16.
+__device__ __forceinline__ void unpack4_bfp8_bf16(uint32_t c, uint32_t w[2]) {
+  const uint32_t a = c & 0x7f7f7f7fu;
+  const uint32_t f0 = __float_as_uint((float)(a & 0xffu));
+  const uint32_t f1 = __float_as_uint((float)((a >> 8) & 0xffu));
+  const uint32_t f2 = __float_as_uint((float)((a >> 16) & 0xffu));
+  const uint32_t f3 = __float_as_uint((float)(a >> 24));
+  // byte selectors: result = [hi16(second) : hi16(first)]
+  w[0] = __builtin_amdgcn_perm(f2, f0, 0x07060302u) | ((c << 8) & 0x80008000u);
+  w[1] = __builtin_amdgcn_perm(f3, f1, 0x07060302u) | (c & 0x80008000u);
+}
+
+// acc + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
 }
 
 // Multiplier applied to a block's unpacked integers: 2^(E - kScaleBias). Exact for every
