@@ -72,8 +72,10 @@ _SIGS = {
     "bfp_gemm": (ctypes.c_int32, [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
+    "bfp_moe_route_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_MoeLayer), ctypes.c_int64]),
     "bfp_moe_route": (ctypes.c_int32, [ctypes.POINTER(_MoeLayer), ctypes.c_void_p, ctypes.c_int64,
-                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p]),
     "bfp_moe_dispatch": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "bfp_moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_MoeLayer), ctypes.c_int64]),
@@ -235,8 +237,10 @@ def bfp_moe_route(layer: MoeLayer, x: torch.Tensor, stream=None):
     w = torch.empty((m, layer.top_k), dtype=torch.float32, device=x.device)
     g = torch.empty((m,), dtype=torch.float32, device=x.device)
     v = layer.view()
+    need = int(lib().bfp_moe_route_workspace_bytes(ctypes.byref(v), m))
+    ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
     _check("bfp_moe_route", lib().bfp_moe_route(ctypes.byref(v), _ptr(x), m, _ptr(ids), _ptr(w), _ptr(g),
-                                                _stream(stream)))
+                                                _ptr(ws), ws.numel(), _stream(stream)))
     return ids, w, g
 
 

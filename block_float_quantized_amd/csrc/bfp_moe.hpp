@@ -1,0 +1,69 @@
+// Internal interface of the MoE kernels (routing, dispatch, grouped expert matmuls, combine).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bfp {
+
+struct RouteArgs {
+  const uint16_t* x;           // bf16 [m][hidden]
+  int m, hidden;
+  const uint16_t* router_w;    // bf16 [n_exp][hidden]
+  const float* bias;           // fp32 [n_exp] or null
+  const uint16_t* sh_gate_w;   // bf16 [hidden] or null
+  int n_exp, top_k;
+  double* logits;              // fp64 [m][ld_logits] (n_exp + 1 columns)
+  int ld_logits;
+  int32_t* ids;                // [m][top_k]
+  float* w;                    // [m][top_k]
+  float* g;                    // [m] or null
+};
+hipError_t router_launch(const RouteArgs& a, hipStream_t s);
+
+struct DispatchArgs {
+  const int32_t* ids;          // [m][top_k]
+  int m, top_k, n_exp;
+  int32_t* counts;             // [n_exp]
+  int32_t* offsets;            // [n_exp + 1]
+  int32_t* perm;               // [m * top_k]
+  int32_t* inv;                // [m * top_k] position of each pair in perm, or null
+  int32_t* active;             // [n_exp] experts with count > 0, ascending, or null
+  int32_t* n_active;           // [1] or null
+};
+hipError_t dispatch_launch(const DispatchArgs& a, hipStream_t s);
+
+// Expert-grouped skinny matmul for decode: workgroup row y picks the y-th active expert (or
+// the shared expert right after the active ones) and streams that expert's rows once for all
+// of its (token, slot) pairs.
+struct MoeGemvArgs {
+  const uint8_t *exp0, *code0, *exp1, *code1;       // routed experts, stacked along rows
+  const uint8_t *sexp0, *scode0, *sexp1, *scode1;   // shared expert (null: none)
+  int rows_per_expert;                              // N of one expert
+  int k;                                            // K
+  const int32_t* active;
+  const int32_t* n_active;
+  const int32_t* offsets;
+  const int32_t* perm;
+  int m, top_k;
+  const void* x;                                    // x bf16 [m][k] (by token) or h fp32 [pairs][k]
+  int64_t ldx;
+  int x_by_token;                                   // 1: read the pair's token row, 0: its position row
+  int x_bf16;
+  void* y;                                          // [pairs][ldy], row = pair position
+  int64_t ldy;
+  int y_bf16;
+};
+hipError_t moe_gemv_launch(const MoeGemvArgs& a, int nmat, hipStream_t s);
+
+struct CombineArgs {
+  const float* o;              // [m*top_k + m][hidden] per-pair expert outputs (+ shared rows)
+  const int32_t* inv;          // [m*top_k]
+  const float* w;              // [m][top_k]
+  const float* g;              // [m] (shared gate) or null when there is no shared expert
+  int m, top_k, hidden;
+  float* y;                    // [m][hidden]
+};
+hipError_t combine_launch(const CombineArgs& a, hipStream_t s);
+
+}  // namespace bfp

@@ -1,0 +1,33 @@
+// Internal interface of the MoE prefill path (expert-grouped bf16 matrix-core GEMMs).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/libbfp.h"
+
+namespace bfp {
+
+struct PrefillArgs {
+  const bfp_moe_layer* L;
+  const uint16_t* x;          // bf16 [m][hidden]
+  int m;
+  float* y;                   // [m][hidden]
+  const float* w;             // [m][top_k] routing weights
+  const float* g;             // [m] shared gate, or null without a shared expert
+  const int32_t* inv;         // [m*top_k] position of each pair in perm
+  const int32_t* perm;        // [m*top_k] pairs sorted by (expert, token)
+  const int32_t* offsets;     // [E+1]
+  const int32_t* counts;      // [E]
+  const int32_t* active;      // [E]
+  const int32_t* n_active;    // [1]
+  uint16_t* h;                // bf16 [m*top_k + m][inter]
+  float* o;                   // fp32 [m*top_k + m][hidden]
+  char* extra;                // prefill_workspace_extra_bytes(m, E, top_k) bytes
+};
+
+size_t prefill_workspace_extra_bytes(int m, int n_exp, int top_k);
+hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s);
+
+}  // namespace bfp

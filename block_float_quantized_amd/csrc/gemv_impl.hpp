@@ -82,8 +82,10 @@ __device__ __forceinline__ uint32_t load_exps(const uint8_t* exp, int64_t row, i
 }
 
 // Stage x[:, kc0:kc0+kcn) into LDS (rows >= m are zero).
+// Activation row of slot mi: xrow[mi] when a row list is given (gathered rows), else mi.
 template <int FMT, int MB, bool XB, int UVALS, int kThreads>
-__device__ __forceinline__ void stage_x(uint32_t* xs, const void* x, int64_t ldx, int m, int kc0, int kcn) {
+__device__ __forceinline__ void stage_x(uint32_t* xs, const void* x, int64_t ldx, int m, int kc0, int kcn,
+                                        const int* xrow) {
   using L = XLayout<XB, UVALS>;
   const int nuc = kcn / UVALS;
   if constexpr (XB) {
@@ -94,7 +96,8 @@ __device__ __forceinline__ void stage_x(uint32_t* xs, const void* x, int64_t ldx
       const int mi = idx / per_row, c8 = idx % per_row;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (mi < m)
-        v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + mi * ldx + kc0 + c8 * 8);
+        v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (int64_t)(xrow ? xrow[mi] : mi) * ldx +
+                                            kc0 + c8 * 8);
       uint4 o;
       if constexpr (FMT == 4) {
         o.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);   // (x0, x2)
@@ -117,7 +120,8 @@ __device__ __forceinline__ void stage_x(uint32_t* xs, const void* x, int64_t ldx
       const int mi = idx / per_row, c4 = idx % per_row;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (mi < m)
-        v = *reinterpret_cast<const uint4*>(static_cast<const float*>(x) + mi * ldx + kc0 + c4 * 4);
+        v = *reinterpret_cast<const uint4*>(static_cast<const float*>(x) + (int64_t)(xrow ? xrow[mi] : mi) * ldx +
+                                            kc0 + c4 * 4);
       const int kk = c4 * 4;
       *reinterpret_cast<uint4*>(xs + ((size_t)mi * nuc + kk / UVALS) * L::kStrideDw + (kk % UVALS)) = v;
     }
@@ -254,9 +258,13 @@ __device__ __forceinline__ void compute_group(float (&acc)[NMAT][RT][MB], const 
 // matrices NMAT, units per group U, blocks per unit BPU, bf16 activations XB, threads per
 // workgroup). When a chunk holds more than one group per lane, the next group's loads are
 // issued before the current group's arithmetic (two register buffers).
+//
+// gemv_tile computes the rows [row_base, row_base + rows per workgroup) of one matrix view for
+// a.m activation rows; xrow/yrow (in LDS, or null for the identity) map activation slot i to
+// the row of x it reads and the row of y it writes.
 template <int FMT, int MB, int RT, int LPR, int NMAT, int U, int BPU, bool XB, int kThreads>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
-  extern __shared__ uint32_t xs[];
+__device__ __forceinline__ void gemv_tile(const GemvArgs& a, int row_base, const int* xrow, const int* yrow,
+                                          uint32_t* xs) {
   using UT = Unit<FMT, BPU>;
   using GroupT = Group<FMT, BPU, U, NMAT, RT>;
   constexpr int G = kWave / LPR;           // lane groups per wave
@@ -267,8 +275,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   const int wave = threadIdx.x / kWave;
   const int grp = lane / LPR;
   const int p = lane % LPR;
-  const int rows_per_wg = (kThreads / kWave) * G * RT;
-  const int row0 = blockIdx.x * rows_per_wg + (wave * G + grp) * RT;
+  const int row0 = row_base + (wave * G + grp) * RT;
 
   const uint8_t* expm[2] = {a.exp0, a.exp1};
   const uint8_t* codem[2] = {a.code0, a.code1};
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     // the first weights are in flight while the activations are staged
     load_group<FMT, BPU, U, NMAT, RT, LPR>(ga, codem, expm, rowc, a.k, nbk, ub0, 0, p, nuc);
     __syncthreads();
-    stage_x<FMT, MB, XB, UT::kValues, kThreads>(xs, a.x, a.ldx, a.m, kc0, kcn);
+    stage_x<FMT, MB, XB, UT::kValues, kThreads>(xs, a.x, a.ldx, a.m, kc0, kcn, xrow);
     __syncthreads();
     {
       GroupT gb;
@@ -339,11 +346,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
       const float g = v[q], u = v[q + 1];
       out = g / (1.0f + __expf(-g)) * u;
     }
+    const int64_t yo = (int64_t)(yrow ? yrow[i] : i) * a.ldy + row;
     if (a.y_bf16)
-      static_cast<uint16_t*>(a.y)[(int64_t)i * a.ldy + row] = (uint16_t)f32_to_bf16_rne(out);
+      static_cast<uint16_t*>(a.y)[yo] = (uint16_t)f32_to_bf16_rne(out);
     else
-      static_cast<float*>(a.y)[(int64_t)i * a.ldy + row] = out;
+      static_cast<float*>(a.y)[yo] = out;
   }
+}
+
+template <int FMT, int MB, int RT, int LPR, int NMAT, int U, int BPU, bool XB, int kThreads>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
+  extern __shared__ uint32_t xs[];
+  constexpr int rows_per_wg = (kThreads / kWave) * (kWave / LPR) * RT;
+  gemv_tile<FMT, MB, RT, LPR, NMAT, U, BPU, XB, kThreads>(a, blockIdx.x * rows_per_wg, nullptr, nullptr, xs);
 }
 
 // ---- launch selection (host) --------------------------------------------------------------

@@ -1,23 +1,208 @@
-// C ABI of the MoE entry points (placeholder until the MoE kernels land).
+// C ABI of the MoE entry points: layer checks, workspace layout, and the decode pipeline
+// (route -> dispatch -> grouped gate/up + SwiGLU -> grouped down -> combine).
 #include <hip/hip_runtime.h>
 
 #include "../../include/libbfp.h"
+#include "bfp_moe.hpp"
+#include "bfp_prefill.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_mat(const bfp_tensor& t, int64_t n, int64_t k) {
+  if (t.fmt != BFP_FMT_BFP4) return t.fmt == BFP_FMT_BFP8 ? BFP_E_UNSUPPORTED : BFP_E_ARG;
+  if (t.n != n || t.k != k) return BFP_E_SHAPE;
+  if (!t.exp || !t.code) return BFP_E_ARG;
+  if (!aligned16(t.exp) || !aligned16(t.code)) return BFP_E_ALIGN;
+  return BFP_OK;
+}
+
+int32_t check_router(const bfp_moe_layer* L) {
+  if (!L) return BFP_E_ARG;
+  if (L->n_experts < 1 || L->n_experts > 256) return BFP_E_SHAPE;
+  if (L->top_k < 1 || L->top_k > 8 || L->top_k > L->n_experts) return BFP_E_SHAPE;
+  if (L->hidden <= 0 || L->hidden % 32 != 0 || L->hidden > (1 << 16)) return BFP_E_SHAPE;
+  if (!L->router_w) return BFP_E_ARG;
+  if (!aligned16(L->router_w) || (L->sh_gate_w && !aligned16(L->sh_gate_w))) return BFP_E_ALIGN;
+  return BFP_OK;
+}
+
+int32_t check_layer(const bfp_moe_layer* L) {
+  int32_t st = check_router(L);
+  if (st != BFP_OK) return st;
+  if (L->inter <= 0 || L->inter % 32 != 0 || L->inter > (1 << 16)) return BFP_E_SHAPE;
+  const int64_t E = L->n_experts, H = L->hidden, F = L->inter;
+  if ((st = check_mat(L->gate, E * F, H)) != BFP_OK) return st;
+  if ((st = check_mat(L->up, E * F, H)) != BFP_OK) return st;
+  if ((st = check_mat(L->down, E * H, F)) != BFP_OK) return st;
+  if (L->sh_gate.fmt != 0) {
+    if ((st = check_mat(L->sh_gate, F, H)) != BFP_OK) return st;
+    if ((st = check_mat(L->sh_up, F, H)) != BFP_OK) return st;
+    if ((st = check_mat(L->sh_down, H, F)) != BFP_OK) return st;
+  }
+  return BFP_OK;
+}
+
+// Workspace regions, each 256-byte aligned.
+struct Layout {
+  size_t logits, ids, w, g, counts, offsets, perm, inv, active, nact, h, o, extra, total;
+};
+
+size_t place(size_t& off, size_t bytes) {
+  const size_t at = off;
+  off += (bytes + 255) / 256 * 256;
+  return at;
+}
+
+Layout layout(const bfp_moe_layer* L, int64_t m, bool with_experts) {
+  Layout y{};
+  size_t off = 0;
+  const int64_t E = L->n_experts, K = L->top_k, H = L->hidden, F = L->inter;
+  const int64_t pairs = m * K + m;
+  const bool prefill = m > BFP_GEMM_MAX_M;
+  y.logits = place(off, (size_t)m * (E + 1) * sizeof(double));
+  if (with_experts) {
+    y.ids = place(off, (size_t)m * K * 4);
+    y.w = place(off, (size_t)m * K * 4);
+    y.g = place(off, (size_t)m * 4);
+    y.counts = place(off, (size_t)E * 4);
+    y.offsets = place(off, (size_t)(E + 1) * 4);
+    y.perm = place(off, (size_t)m * K * 4);
+    y.inv = place(off, (size_t)m * K * 4);
+    y.active = place(off, (size_t)E * 4);
+    y.nact = place(off, 16);
+    if (prefill) {
+      y.h = place(off, (size_t)pairs * F * 2);       // bf16 h
+      y.o = place(off, (size_t)pairs * H * 4);
+      y.extra = off;
+      y.total = off + bfp::prefill_workspace_extra_bytes((int)m, (int)E, (int)K);
+      return y;
+    }
+    y.h = place(off, (size_t)pairs * F * 4);
+    y.o = place(off, (size_t)pairs * H * 4);
+  }
+  y.total = off;
+  return y;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+int32_t from_hip(hipError_t e) { return e == hipSuccess ? BFP_OK : BFP_E_DEVICE; }
+
+bfp::RouteArgs route_args(const bfp_moe_layer* L, const uint16_t* x, int64_t m, double* logits, int32_t* ids,
+                          float* w, float* g) {
+  bfp::RouteArgs r;
+  r.x = x; r.m = (int)m; r.hidden = (int)L->hidden;
+  r.router_w = L->router_w; r.bias = L->router_bias; r.sh_gate_w = L->sh_gate_w;
+  r.n_exp = L->n_experts; r.top_k = L->top_k;
+  r.logits = logits; r.ld_logits = L->n_experts + 1;
+  r.ids = ids; r.w = w; r.g = g;
+  return r;
+}
+
+}  // namespace
 
 extern "C" {
 
-int32_t bfp_moe_route(const bfp_moe_layer*, const uint16_t*, int64_t, int32_t*, float*, float*, void*) {
-  return BFP_E_UNSUPPORTED;
+size_t bfp_moe_route_workspace_bytes(const bfp_moe_layer* L, int64_t m) {
+  if (check_router(L) != BFP_OK || m < 1 || m > BFP_MOE_MAX_M) return 0;
+  return layout(L, m, false).total;
 }
 
-int32_t bfp_moe_dispatch(const int32_t*, int64_t, int32_t, int32_t, int32_t*, int32_t*, int32_t*, void*) {
-  return BFP_E_UNSUPPORTED;
+int32_t bfp_moe_route(const bfp_moe_layer* L, const uint16_t* x, int64_t m, int32_t* ids, float* w, float* g,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_router(L);
+  if (st != BFP_OK) return st;
+  if (m < 1 || m > BFP_MOE_MAX_M) return BFP_E_SHAPE;
+  if (!x || !ids || !w) return BFP_E_ARG;
+  if (!aligned16(x)) return BFP_E_ALIGN;
+  const Layout y = layout(L, m, false);
+  if (!ws || ws_bytes < y.total) return BFP_E_WORKSPACE;
+  if (!aligned16(ws)) return BFP_E_ALIGN;
+  return from_hip(bfp::router_launch(route_args(L, x, m, at<double>(ws, y.logits), ids, w, g),
+                                     static_cast<hipStream_t>(stream)));
 }
 
-size_t bfp_moe_workspace_bytes(const bfp_moe_layer*, int64_t) { return 0; }
+int32_t bfp_moe_dispatch(const int32_t* ids, int64_t m, int32_t top_k, int32_t n_experts, int32_t* counts,
+                         int32_t* offsets, int32_t* perm, void* stream) {
+  if (!ids || !counts || !offsets || !perm) return BFP_E_ARG;
+  if (m < 1 || m > BFP_MOE_MAX_M || top_k < 1 || top_k > 8 || n_experts < 1 || n_experts > 256 ||
+      top_k > n_experts)
+    return BFP_E_SHAPE;
+  bfp::DispatchArgs d{};
+  d.ids = ids; d.m = (int)m; d.top_k = top_k; d.n_exp = n_experts;
+  d.counts = counts; d.offsets = offsets; d.perm = perm;
+  return from_hip(bfp::dispatch_launch(d, static_cast<hipStream_t>(stream)));
+}
 
-int32_t bfp_moe_forward(const bfp_moe_layer*, const uint16_t*, int64_t, float*, int32_t*, float*, void*,
-                        size_t, void*) {
-  return BFP_E_UNSUPPORTED;
+size_t bfp_moe_workspace_bytes(const bfp_moe_layer* L, int64_t m) {
+  if (check_layer(L) != BFP_OK || m < 1 || m > BFP_MOE_MAX_M) return 0;
+  return layout(L, m, true).total;
+}
+
+int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, float* y, int32_t* topk_ids,
+                        float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_layer(L);
+  if (st != BFP_OK) return st;
+  if (m < 1 || m > BFP_MOE_MAX_M) return BFP_E_SHAPE;
+  if (!x || !y) return BFP_E_ARG;
+  if (!aligned16(x) || !aligned16(y)) return BFP_E_ALIGN;
+  const Layout ly = layout(L, m, true);
+  if (!ws || ws_bytes < ly.total) return BFP_E_WORKSPACE;
+  if (!aligned16(ws)) return BFP_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool shared = L->sh_gate.fmt != 0;
+  int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, ly.ids);
+  float* w = topk_w ? topk_w : at<float>(ws, ly.w);
+  float* g = at<float>(ws, ly.g);
+  hipError_t e = bfp::router_launch(route_args(L, x, m, at<double>(ws, ly.logits), ids, w, g), s);
+  if (e != hipSuccess) return BFP_E_DEVICE;
+  bfp::DispatchArgs d{};
+  d.ids = ids; d.m = (int)m; d.top_k = L->top_k; d.n_exp = L->n_experts;
+  d.counts = at<int32_t>(ws, ly.counts); d.offsets = at<int32_t>(ws, ly.offsets);
+  d.perm = at<int32_t>(ws, ly.perm); d.inv = at<int32_t>(ws, ly.inv);
+  d.active = at<int32_t>(ws, ly.active); d.n_active = at<int32_t>(ws, ly.nact);
+  if ((e = bfp::dispatch_launch(d, s)) != hipSuccess) return BFP_E_DEVICE;
+
+  if (m > BFP_GEMM_MAX_M) {
+    bfp::PrefillArgs p{};
+    p.L = L; p.x = x; p.m = (int)m; p.y = y;
+    p.w = w; p.g = shared ? g : nullptr; p.inv = d.inv; p.perm = d.perm; p.offsets = d.offsets;
+    p.counts = d.counts; p.active = d.active; p.n_active = d.n_active;
+    p.h = at<uint16_t>(ws, ly.h); p.o = at<float>(ws, ly.o);
+    p.extra = at<char>(ws, ly.extra);
+    return from_hip(bfp::prefill_launch(p, s));
+  }
+
+  float* h = at<float>(ws, ly.h);
+  float* o = at<float>(ws, ly.o);
+  bfp::MoeGemvArgs gu{};
+  gu.exp0 = L->gate.exp; gu.code0 = L->gate.code; gu.exp1 = L->up.exp; gu.code1 = L->up.code;
+  if (shared) {
+    gu.sexp0 = L->sh_gate.exp; gu.scode0 = L->sh_gate.code; gu.sexp1 = L->sh_up.exp; gu.scode1 = L->sh_up.code;
+  }
+  gu.rows_per_expert = (int)L->inter; gu.k = (int)L->hidden;
+  gu.active = d.active; gu.n_active = d.n_active; gu.offsets = d.offsets; gu.perm = d.perm;
+  gu.m = (int)m; gu.top_k = L->top_k;
+  gu.x = x; gu.ldx = L->hidden; gu.x_by_token = 1; gu.x_bf16 = 1;
+  gu.y = h; gu.ldy = L->inter; gu.y_bf16 = 0;
+  if ((e = bfp::moe_gemv_launch(gu, 2, s)) != hipSuccess) return BFP_E_DEVICE;
+
+  bfp::MoeGemvArgs dn = gu;
+  dn.exp0 = L->down.exp; dn.code0 = L->down.code; dn.exp1 = nullptr; dn.code1 = nullptr;
+  dn.sexp0 = shared ? L->sh_down.exp : nullptr; dn.scode0 = shared ? L->sh_down.code : nullptr;
+  dn.sexp1 = nullptr; dn.scode1 = nullptr;
+  dn.rows_per_expert = (int)L->hidden; dn.k = (int)L->inter;
+  dn.x = h; dn.ldx = L->inter; dn.x_by_token = 0; dn.x_bf16 = 0;
+  dn.y = o; dn.ldy = L->hidden; dn.y_bf16 = 0;
+  if ((e = bfp::moe_gemv_launch(dn, 1, s)) != hipSuccess) return BFP_E_DEVICE;
+
+  bfp::CombineArgs c{};
+  c.o = o; c.inv = d.inv; c.w = w; c.g = shared ? g : nullptr;
+  c.m = (int)m; c.top_k = L->top_k; c.hidden = (int)L->hidden; c.y = y;
+  return from_hip(bfp::combine_launch(c, s));
 }
 
 }  // extern "C"

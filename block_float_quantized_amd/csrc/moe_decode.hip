@@ -1,0 +1,142 @@
+// Expert-grouped skinny BFP4 matmuls and the weighted combine for MoE decode (gfx950).
+//
+// "Qwen3.6-35B-A3B — TT-native mixed BFP4/BFP8", section "Fused decode kernels": MoE decode
+// runs through device top-k routing and batched expert streams, one gate/up and one down
+// program for all rows; "Qwen3.8-27B ...", "Multi-user decode": every weight is read once per
+// step for all rows. Here each selected expert's rows are streamed once by the same kernel
+// tile as the dense GEMV, for all (token, slot) pairs routed to it; the shared expert is one
+// more group with every token. The combine then forms y_t = sum_j w_tj o_tj (slots in rank
+// order) + g_t * shared_t, a fixed order, so the result does not depend on scheduling.
+#include "bfp_moe.hpp"
+#include "gemv_impl.hpp"
+
+namespace bfp {
+
+namespace {
+
+using namespace gemv_detail;
+
+constexpr int kMoeThreads = 256;
+
+inline __host__ __device__ int mb_bucket(int n) {
+  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : 32;
+}
+
+template <int NMAT, bool XB, int MB, int LPR>
+__device__ __forceinline__ void run_tile(const GemvArgs& a, int row_base, const int* xrow, const int* yrow,
+                                         uint32_t* xs) {
+  constexpr int U = MB <= 4 ? 2 : 1;
+  gemv_tile<4, MB, 1, LPR, NMAT, U, 2, XB, kMoeThreads>(a, row_base, xrow, yrow, xs);
+}
+
+template <int NMAT, bool XB, int MBMAX, int LPR>
+__global__ __launch_bounds__(kMoeThreads) void moe_gemv_kernel(MoeGemvArgs ma, int kc) {
+  extern __shared__ uint32_t xs[];
+  __shared__ int xrow[32], yrow[32];
+  const int d = blockIdx.y;
+  const int na = *ma.n_active;
+  const bool shared = d == na && ma.scode0 != nullptr;
+  if (d > na || (d == na && !shared)) return;
+  int e = -1, p0, n;
+  if (!shared) {
+    e = ma.active[d];
+    p0 = ma.offsets[e];
+    n = ma.offsets[e + 1] - p0;
+  } else {
+    p0 = ma.m * ma.top_k;
+    n = ma.m;
+  }
+  if ((int)threadIdx.x < n) {
+    const int pos = p0 + threadIdx.x;
+    const int tok = shared ? (int)threadIdx.x : ma.perm[pos] / ma.top_k;
+    xrow[threadIdx.x] = ma.x_by_token ? tok : pos;
+    yrow[threadIdx.x] = pos;
+  }
+  GemvArgs a;
+  const int64_t nbk = ma.k / kBlock;
+  const int64_t rows0 = shared ? 0 : (int64_t)e * ma.rows_per_expert;
+  a.exp0 = (shared ? ma.sexp0 : ma.exp0) + rows0 * nbk;
+  a.code0 = (shared ? ma.scode0 : ma.code0) + rows0 * (ma.k / 2);
+  a.exp1 = NMAT == 2 ? (shared ? ma.sexp1 : ma.exp1) + rows0 * nbk : nullptr;
+  a.code1 = NMAT == 2 ? (shared ? ma.scode1 : ma.code1) + rows0 * (ma.k / 2) : nullptr;
+  a.x = ma.x; a.ldx = ma.ldx;
+  a.y = ma.y; a.ldy = ma.ldy; a.y_bf16 = ma.y_bf16;
+  a.n = ma.rows_per_expert; a.k = ma.k; a.m = n; a.kc = kc;
+  constexpr int RPW = (kMoeThreads / kWave) * (kWave / LPR);
+  const int row_base = blockIdx.x * RPW;
+  // xrow/yrow are read after the first barrier inside the tile
+  switch (mb_bucket(n)) {
+    case 1: run_tile<NMAT, XB, 1, LPR>(a, row_base, xrow, yrow, xs); break;
+    case 2: if constexpr (MBMAX >= 2) run_tile<NMAT, XB, 2, LPR>(a, row_base, xrow, yrow, xs); break;
+    case 4: if constexpr (MBMAX >= 4) run_tile<NMAT, XB, 4, LPR>(a, row_base, xrow, yrow, xs); break;
+    case 8: if constexpr (MBMAX >= 8) run_tile<NMAT, XB, 8, LPR>(a, row_base, xrow, yrow, xs); break;
+    case 16: if constexpr (MBMAX >= 16) run_tile<NMAT, XB, 16, LPR>(a, row_base, xrow, yrow, xs); break;
+    default: if constexpr (MBMAX >= 32) run_tile<NMAT, XB, 32, LPR>(a, row_base, xrow, yrow, xs); break;
+  }
+}
+
+template <int NMAT, bool XB, int MBMAX>
+hipError_t launch_mbmax(const MoeGemvArgs& ma, hipStream_t s) {
+  constexpr int LPR = 16;
+  using L = XLayout<XB, 32>;
+  const int kc = pick_kc(ma.k, MBMAX, 32, LPR, L::kBytesPerValue);
+  const size_t lds = (size_t)MBMAX * (kc / 32) * L::kStrideDw * sizeof(uint32_t);
+  constexpr int RPW = (kMoeThreads / kWave) * (kWave / LPR);
+  const int groups = (ma.m * ma.top_k < 256 ? ma.m * ma.top_k : 256) + (ma.scode0 ? 1 : 0);
+  dim3 grid((ma.rows_per_expert + RPW - 1) / RPW, groups);
+  hipLaunchKernelGGL((moe_gemv_kernel<NMAT, XB, MBMAX, LPR>), grid, dim3(kMoeThreads), lds, s, ma, kc);
+  return hipGetLastError();
+}
+
+template <int NMAT, bool XB>
+hipError_t launch_x(const MoeGemvArgs& ma, hipStream_t s) {
+  switch (mb_bucket(ma.m)) {
+    case 1: return launch_mbmax<NMAT, XB, 1>(ma, s);
+    case 2: return launch_mbmax<NMAT, XB, 2>(ma, s);
+    case 4: return launch_mbmax<NMAT, XB, 4>(ma, s);
+    case 8: return launch_mbmax<NMAT, XB, 8>(ma, s);
+    case 16: return launch_mbmax<NMAT, XB, 16>(ma, s);
+    default: return launch_mbmax<NMAT, XB, 32>(ma, s);
+  }
+}
+
+// y[t][n] = sum_j w[t][j] * o[inv[t*K+j]][n] + g[t] * o[m*K + t][n]; four outputs per thread.
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int t = blockIdx.y;
+  const int n4 = blockIdx.x * 256 + threadIdx.x;
+  if (n4 * 4 >= a.hidden) return;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < a.top_k; ++j) {
+    const float wj = a.w[(int64_t)t * a.top_k + j];
+    const int pos = a.inv[(int64_t)t * a.top_k + j];
+    const f32x4 o = *reinterpret_cast<const f32x4*>(a.o + (int64_t)pos * a.hidden + n4 * 4);
+    acc.x = __builtin_fmaf(wj, o.x, acc.x);
+    acc.y = __builtin_fmaf(wj, o.y, acc.y);
+    acc.z = __builtin_fmaf(wj, o.z, acc.z);
+    acc.w = __builtin_fmaf(wj, o.w, acc.w);
+  }
+  if (a.g) {
+    const float gt = a.g[t];
+    const f32x4 o = *reinterpret_cast<const f32x4*>(a.o + ((int64_t)a.m * a.top_k + t) * a.hidden + n4 * 4);
+    acc.x = __builtin_fmaf(gt, o.x, acc.x);
+    acc.y = __builtin_fmaf(gt, o.y, acc.y);
+    acc.z = __builtin_fmaf(gt, o.z, acc.z);
+    acc.w = __builtin_fmaf(gt, o.w, acc.w);
+  }
+  *reinterpret_cast<f32x4*>(a.y + (int64_t)t * a.hidden + n4 * 4) = acc;
+}
+
+}  // namespace
+
+hipError_t moe_gemv_launch(const MoeGemvArgs& a, int nmat, hipStream_t s) {
+  if (nmat == 2) return a.x_bf16 ? launch_x<2, true>(a, s) : launch_x<2, false>(a, s);
+  return a.x_bf16 ? launch_x<1, true>(a, s) : launch_x<1, false>(a, s);
+}
+
+hipError_t combine_launch(const CombineArgs& a, hipStream_t s) {
+  dim3 grid((a.hidden / 4 + 255) / 256, a.m);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bfp

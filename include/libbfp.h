@@ -133,14 +133,17 @@ int32_t bfp_gemm(const bfp_tensor *w, const bfp_tensor *w_up, int32_t epilogue,
 typedef struct bfp_moe_layer {
   int32_t n_experts;      /* routed experts, 1..256 */
   int32_t top_k;          /* experts per token, 1..8 */
-  int64_t hidden;         /* model width (multiple of 16) */
-  int64_t inter;          /* expert width (multiple of 16) */
+  int64_t hidden;         /* model width (multiple of 32) */
+  int64_t inter;          /* expert width (multiple of 32) */
   const uint16_t *router_w;
   const float *router_bias;
   bfp_tensor gate, up, down;
   bfp_tensor sh_gate, sh_up, sh_down;
   const uint16_t *sh_gate_w;
 } bfp_moe_layer;
+
+/* Workspace bytes bfp_moe_route needs for m tokens (the fp64 router logits). */
+size_t bfp_moe_route_workspace_bytes(const bfp_moe_layer *L, int64_t m);
 
 /*
  * Routing step of bfp_moe_forward, exposed on its own. For each token t < m:
@@ -151,10 +154,11 @@ typedef struct bfp_moe_layer {
  *             (= exp(l_ej - l_max) / sum over the selection), fp32;
  *   g[t] = sigmoid(x[t] . sh_gate_w) (1 if sh_gate_w is NULL), fp32.
  * x: device bf16 [m][hidden]; ids: device int32 [m][top_k]; w: device fp32 [m][top_k];
- * g: device fp32 [m] or NULL.
+ * g: device fp32 [m] or NULL; ws: device workspace of at least
+ * bfp_moe_route_workspace_bytes(L, m) bytes. Only the router fields of L are read.
  */
 int32_t bfp_moe_route(const bfp_moe_layer *L, const uint16_t *x, int64_t m,
-                      int32_t *ids, float *w, float *g, void *stream);
+                      int32_t *ids, float *w, float *g, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Dispatch structure for expert-grouped execution (counting sort by expert):

@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "rng_for", "bf16_bits", "bf16_values", "normal_bf16", "dense_weights",
-    "gemv_case", "mlp_case", "proj_case", "moe_layer", "moe_tokens", "router_bias",
+    "gemv_case", "mlp_case", "proj_case", "moe_router", "moe_layer", "moe_tokens", "router_bias",
     "HIDDEN", "INTER", "N_EXPERTS", "TOP_K",
 ]
 
@@ -115,6 +115,13 @@ def proj_case(m: int, seed: int = 0, hidden: int = 2048, q_out: int = 4096, kv_o
     return d
 
 
+def moe_router(seed: int = 0, n_experts: int = N_EXPERTS, hidden: int = HIDDEN):
+    """Router bf16 [E][hidden] N(0, 0.02) and shared-expert gate vector bf16 [hidden]."""
+    router = normal_bf16(rng_for(seed, 4, "router"), (n_experts, hidden), std=0.02)
+    sh_gate_w = normal_bf16(rng_for(seed, 4, "shared_gate"), (hidden,), std=0.02)
+    return router, sh_gate_w
+
+
 def moe_layer(seed: int = 0, n_experts: int = N_EXPERTS, hidden: int = HIDDEN, inter: int = INTER,
               experts: np.ndarray | None = None) -> dict:
     """One MoE layer: bf16 router [E][hidden], stacked expert weights, shared expert.
@@ -126,8 +133,7 @@ def moe_layer(seed: int = 0, n_experts: int = N_EXPERTS, hidden: int = HIDDEN, i
     CPU tests build the few experts they route to without drawing all 256.
     """
     cfg = 4  # the decode and prefill workloads share one layer
-    router = normal_bf16(rng_for(seed, cfg, "router"), (n_experts, hidden), std=0.02)
-    sh_gate_w = normal_bf16(rng_for(seed, cfg, "shared_gate"), (hidden,), std=0.02)
+    router, sh_gate_w = moe_router(seed, n_experts, hidden)
     scales = rng_for(seed, cfg, "expert_scale").lognormal(0.0, 0.3, size=n_experts + 1).astype(np.float32)
     sel = np.arange(n_experts) if experts is None else np.unique(np.asarray(experts, dtype=np.int64))
     gate = np.zeros((n_experts * inter, hidden), np.float32)

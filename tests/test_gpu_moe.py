@@ -1,0 +1,107 @@
+"""GPU MoE routing, dispatch and layer forward against the oracle.
+
+Routing and dispatch are integer decisions and must match bit for bit (expert ids and
+their order, counts, offsets, permutation). Routing weights and the shared gate are fp32
+outputs of fp64 computations (within 1e-6 relative). The layer output y is within 2e-3 of
+the oracle's, relative to the oracle's sum of |w_j| * sum_k |h_k Wd_k| (+ the shared term).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_float_quantized_amd as bfq
+import oracle
+import synth
+from gpu_util import assert_within, dev_bf16, dev_f32, note
+from moe_util import LazyBank, device_layer
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _router_only_layer(seed, bias=None):
+    router, shg = synth.moe_router(seed)
+    dummy = bfq.BfpMatrix(4, 1, 32, torch.zeros(16, dtype=torch.uint8, device="cuda"),
+                          torch.zeros(16, dtype=torch.uint8, device="cuda"))
+    lay = bfq.MoeLayer(256, 8, synth.HIDDEN, synth.INTER, dev_bf16(router),
+                       dev_f32(bias) if bias is not None else None, dummy, dummy, dummy, None, None, None,
+                       dev_bf16(shg))
+    return lay, router, shg
+
+
+@pytest.mark.parametrize("m,with_bias", [(1, False), (8, False), (16, False), (32, False), (2048, True)])
+def test_route_matches_oracle(m, with_bias):
+    note(f"route m={m} bias={with_bias}")
+    bias = synth.router_bias(0) if with_bias else None
+    lay, router, shg = _router_only_layer(0, bias)
+    x = synth.moe_tokens(m, 0, cfg_id=5 if with_bias else 4)
+    ids, w, g = bfq.bfp_moe_route(lay, dev_bf16(x))
+    ref = oracle.route(x, router, 8, bias=bias, sh_gate_bits=shg)
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+    assert np.allclose(w.cpu().numpy(), ref["r"], rtol=1e-6, atol=0)
+    assert np.allclose(g.cpu().numpy(), ref["g"], rtol=1e-6, atol=0)
+
+
+def test_route_special_cases():
+    """All-zero router: every logit ties, experts 0..7 in order, weights exactly 1/8."""
+    note("route special cases")
+    lay, router, shg = _router_only_layer(0)
+    lay.router_w = torch.zeros_like(lay.router_w)
+    lay.sh_gate_w = torch.zeros_like(lay.sh_gate_w)
+    x = dev_bf16(synth.moe_tokens(3, 1))
+    ids, w, g = bfq.bfp_moe_route(lay, x)
+    assert ids.cpu().tolist() == [list(range(8))] * 3
+    assert torch.all(w == 0.125) and torch.all(g == 0.5)
+    # a +100 bias on chosen experts forces them, ordered by bias
+    bias = np.zeros(256, np.float32)
+    chosen = [200, 3, 77, 150, 9, 31, 255, 128]
+    for r_, e in enumerate(chosen):
+        bias[e] = 100.0 + 8 - r_
+    lay2, _, _ = _router_only_layer(0, bias)
+    lay2.router_w = torch.zeros_like(lay2.router_w)
+    ids, w, g = bfq.bfp_moe_route(lay2, x)
+    assert ids.cpu().tolist() == [chosen] * 3
+
+
+@pytest.mark.parametrize("m", [1, 7, 300, 2048, 5000])
+def test_dispatch_bit_exact(m):
+    note(f"dispatch m={m}")
+    rng = np.random.default_rng(m)
+    # skewed expert popularity, distinct experts per token
+    p = rng.dirichlet(np.full(256, 0.1))
+    ids = np.stack([rng.choice(256, 8, replace=False, p=p) for _ in range(m)]).astype(np.int32)
+    counts, offsets, perm = bfq.bfp_moe_dispatch(torch.from_numpy(ids).cuda(), 256)
+    ref = oracle.dispatch(ids, 256)
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+
+
+@pytest.fixture(scope="module")
+def moe_full():
+    note("building the 256-expert MoE layer")
+    layer = synth.moe_layer(0)
+    dev = device_layer(layer)
+    return layer, dev, LazyBank(layer)
+
+
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_moe_decode_matches_oracle(moe_full, m):
+    layer, dev, bank = moe_full
+    note(f"moe decode m={m}")
+    x = synth.moe_tokens(m, 0)
+    ids = torch.empty((m, 8), dtype=torch.int32, device="cuda")
+    y = bfq.bfp_moe_forward(dev, dev_bf16(x), topk_ids=ids).cpu().numpy()
+    rt = oracle.route(x, layer["router"], 8, sh_gate_bits=layer["sh_gate_w"])
+    assert np.array_equal(ids.cpu().numpy(), rt["ids"])
+    ref, norm = oracle.moe_decode(bank, x, rt)
+    assert_within(y, ref, norm, TOL, what=f"moe decode m={m}")
+
+
+def test_moe_decode_deterministic_and_row_invariant(moe_full):
+    layer, dev, bank = moe_full
+    note("moe decode determinism")
+    x = dev_bf16(synth.moe_tokens(4, 3))
+    a = bfq.bfp_moe_forward(dev, x)
+    b = bfq.bfp_moe_forward(dev, x)
+    assert torch.equal(a, b)
