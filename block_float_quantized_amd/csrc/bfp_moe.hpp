@@ -30,6 +30,9 @@ struct DispatchArgs {
   int32_t* inv;                // [m * top_k] position of each pair in perm, or null
   int32_t* active;             // [n_exp] experts with count > 0, ascending, or null
   int32_t* n_active;           // [1] or null
+  int tile_m;                  // > 0: also write tile_start for row tiles of tile_m rows
+  int with_shared;             // the tile list ends with a group of all m tokens
+  int32_t* tile_start;         // [n_exp + 2]: first row tile of each group, then the total
 };
 hipError_t dispatch_launch(const DispatchArgs& a, hipStream_t s);
 

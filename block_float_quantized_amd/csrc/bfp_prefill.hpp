@@ -24,10 +24,12 @@ struct PrefillArgs {
   const int32_t* n_active;    // [1]
   uint16_t* h;                // bf16 [m*top_k + m][inter]
   float* o;                   // fp32 [m*top_k + m][hidden]
-  char* extra;                // prefill_workspace_extra_bytes(m, E, top_k) bytes
+  const int32_t* tile_start;  // row-tile list written by the dispatch kernel (tile_m rows)
 };
 
+// Bytes of the tile list, and the row-tile height the dispatch kernel must use for it.
 size_t prefill_workspace_extra_bytes(int m, int n_exp, int top_k);
+int prefill_tile_rows();
 hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s);
 
 }  // namespace bfp

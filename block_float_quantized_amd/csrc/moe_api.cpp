@@ -164,6 +164,11 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
   d.counts = at<int32_t>(ws, ly.counts); d.offsets = at<int32_t>(ws, ly.offsets);
   d.perm = at<int32_t>(ws, ly.perm); d.inv = at<int32_t>(ws, ly.inv);
   d.active = at<int32_t>(ws, ly.active); d.n_active = at<int32_t>(ws, ly.nact);
+  if (m > BFP_GEMM_MAX_M) {
+    d.tile_m = bfp::prefill_tile_rows();
+    d.with_shared = shared;
+    d.tile_start = at<int32_t>(ws, ly.extra);
+  }
   if ((e = bfp::dispatch_launch(d, s)) != hipSuccess) return BFP_E_DEVICE;
 
   if (m > BFP_GEMM_MAX_M) {
@@ -172,7 +177,7 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
     p.w = w; p.g = shared ? g : nullptr; p.inv = d.inv; p.perm = d.perm; p.offsets = d.offsets;
     p.counts = d.counts; p.active = d.active; p.n_active = d.n_active;
     p.h = at<uint16_t>(ws, ly.h); p.o = at<float>(ws, ly.o);
-    p.extra = at<char>(ws, ly.extra);
+    p.tile_start = d.tile_start;
     return from_hip(bfp::prefill_launch(p, s));
   }
 

@@ -1,10 +1,355 @@
-// MoE prefill (placeholder until the grouped matrix-core GEMMs land).
+// MoE prefill for gfx950: expert-grouped GEMMs on the bf16 matrix cores.
+//
+// A 2,048-token prefill chunk ("Qwen3.8-27B — TT-native mixed BFP4/BFP8", section "What
+// changed in this release (s27v6-20261024)": prompts prefill in 2,048-token chunks) routes
+// 16,384 (token, slot) pairs through the 256 BFP4 experts ("qwen3.6-a3b-blackhole",
+// introduction). With the pairs sorted by expert (dispatch), each expert is a dense GEMM:
+//   h = silu(X_e Wg_e^T) * (X_e Wu_e^T)   rounded to bf16,
+//   o = h Wd_e^T                           fp32 per pair,
+// and the shared expert is one more group holding every token. y is then the weighted sum
+// of each token's pair rows (the decode combine kernel).
+//
+// Kernel design:
+//  * One workgroup (4 waves) computes a TM x TN tile of one group. The tile list (row tiles
+//    of every group) comes from the dispatch kernel; workgroups are mapped so that each XCD
+//    takes a contiguous range of tiles, ordered (group, column tile, row tile): the tiles
+//    that reuse one expert's weights share an L2.
+//  * Per K step of 64: the activation rows are gathered (token rows of x, or pair rows of h)
+//    and the BFP4 weight rows are dequantized to bf16 in registers and stored in LDS; the
+//    next step's global loads are issued before the current step's MFMAs.
+//  * v_mfma_f32_16x16x32_bf16 with fp32 accumulation; each wave owns 16 rows of the tile.
+//    A and B share one permutation of K inside every 8-value group (the order the BFP4
+//    unpack produces pairs in), which leaves every dot product unchanged.
+//  * Dequantization is exact: a nibble becomes an FP8 E4M3 subnormal (mag * 2^-9) and the
+//    conversion to bf16 applies the block scale 2^(E-120); blocks whose scale falls outside
+//    the conversion's exact range go through an fp32 path.
+#include "bfp_device.hpp"
+#include "bfp_moe.hpp"
 #include "bfp_prefill.hpp"
 
 namespace bfp {
 
-size_t prefill_workspace_extra_bytes(int, int, int) { return 256; }
+namespace {
 
-hipError_t prefill_launch(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kTM = 64;          // rows (pairs) per tile
+constexpr int kTK = 64;          // K per step
+constexpr int kLDK = kTK + 8;    // bf16 per LDS row (padding spreads banks)
+constexpr int kPT = 256;         // threads per workgroup
+
+struct PfArgs {
+  const uint8_t *exp0, *code0, *exp1, *code1;       // routed (stacked) matrices
+  const uint8_t *sexp0, *scode0, *sexp1, *scode1;   // shared expert
+  int rows_per_expert;                              // N of one expert
+  int k;                                            // K
+  const int32_t* active;
+  const int32_t* n_active;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* tile_start;
+  int with_shared;
+  int m, top_k;
+  const uint16_t* a;                                // A rows (bf16): x by token, or h by position
+  int64_t lda;
+  int a_by_token;
+  void* c;                                          // output rows by pair position
+  int64_t ldc;
+};
+
+// 16 BFP4 values (two dwords) with exponent E -> 8 dwords of bf16 pairs in the permuted order
+// (v0,v2)(v4,v6)(v1,v3)(v5,v7) per 8 values.
+__device__ __forceinline__ void dequant16(uint32_t c0, uint32_t c1, uint32_t e, uint32_t* out) {
+  if (e >= 8 && e <= 247) {
+    const float sc = __uint_as_float((e + 7u) << 23);           // 2^(E - 120)
+    const uint32_t cc[2] = {c0, c1};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = cc[h];
+      const uint32_t ev = ((c << 4) & 0x80808080u) | (c & 0x07070707u);
+      const uint32_t od = (c & 0x80808080u) | ((c >> 4) & 0x07070707u);
+      out[4 * h + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, false));
+      out[4 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, true));
+      out[4 * h + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, false));
+      out[4 * h + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, true));
+    }
+  } else {
+    const int sh = (int)e - 120;
+    float v[16];
+    unpack8_bfp4(c0, v);
+    unpack8_bfp4(c1, v + 8);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* w = v + 8 * h;
+      auto b = [&](int i) { return __float_as_uint(__builtin_amdgcn_ldexpf(w[i], sh)) >> 16; };
+      out[4 * h + 0] = b(0) | (b(2) << 16);
+      out[4 * h + 1] = b(4) | (b(6) << 16);
+      out[4 * h + 2] = b(1) | (b(3) << 16);
+      out[4 * h + 3] = b(5) | (b(7) << 16);
+    }
+  }
+}
+
+// 8 bf16 activations (natural order) -> the same permutation as the weights.
+__device__ __forceinline__ uint4 permute8(uint4 v) {
+  uint4 o;
+  o.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);   // (x0, x2)
+  o.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);   // (x4, x6)
+  o.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);   // (x1, x3)
+  o.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);   // (x5, x7)
+  return o;
+}
+
+struct TileInfo {
+  int shared;       // shared-expert group
+  int e;            // routed expert id
+  int p0, n;        // first pair position and rows of the group
+  int row0;         // first row of the tile inside the group
+  int col0;         // first output column
+};
+
+// Maps this workgroup to a tile; false when it has none. Each XCD (workgroups bid % 8) takes a
+// contiguous range of the tiles that exist.
+template <int TN>
+__device__ __forceinline__ bool find_tile(const PfArgs& a, TileInfo& t) {
+  const int na = *a.n_active;
+  const int ng = na + (a.with_shared ? 1 : 0);
+  const int nct = a.rows_per_expert / TN;
+  const int total = a.tile_start[ng] * nct;
+  const int per = (total + 7) / 8;
+  const int local = blockIdx.x / 8;
+  if (local >= per) return false;
+  const int tile = (blockIdx.x % 8) * per + local;
+  if (tile >= total) return false;
+  // group: last g with tile_start[g] * nct <= tile
+  int lo = 0, hi = ng - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (a.tile_start[mid] * nct <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int g = lo;
+  const int mtiles = a.tile_start[g + 1] - a.tile_start[g];
+  const int loc = tile - a.tile_start[g] * nct;
+  const int ct = loc / mtiles, mt = loc % mtiles;
+  t.shared = g == na;
+  if (t.shared) {
+    t.e = -1;
+    t.p0 = a.m * a.top_k;
+    t.n = a.m;
+  } else {
+    t.e = a.active[g];
+    t.p0 = a.offsets[t.e];
+    t.n = a.offsets[t.e + 1] - t.p0;
+  }
+  t.row0 = mt * kTM;
+  t.col0 = ct * TN;
+  return true;
+}
+
+// Grouped GEMM C[pos][col] = A[row(pos)] . W_e[col] for one tile, NMAT weight matrices of TN
+// rows each. NMAT = 2: SwiGLU of the two (gate, up), stored as bf16; NMAT = 1: fp32 store.
+template <int TN, int NMAT>
+__global__ __launch_bounds__(kPT) void grouped_gemm_kernel(PfArgs a) {
+  __shared__ __align__(16) uint16_t As[kTM][kLDK];
+  __shared__ __align__(16) uint16_t Bs[NMAT][TN][kLDK];
+  __shared__ int arow[kTM];
+  TileInfo t;
+  if (!find_tile<TN>(a, t)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  if (tid < kTM) {
+    const int r = t.row0 + tid;
+    int row = -1;
+    if (r < t.n) {
+      const int pos = t.p0 + r;
+      const int tok = t.shared ? r : a.perm[pos] / a.top_k;
+      row = a.a_by_token ? tok : pos;
+    }
+    arow[tid] = row;
+  }
+  __syncthreads();
+
+  // this thread's share of the global loads of one K step
+  //  A: 64 rows x 64 bf16 = 256 x 32 B: row tid/4, 16 values at (tid%4)*16
+  //  B: NMAT x TN rows x 64 values of BFP4 = 32 B per row: row (tid*?) ...
+  constexpr int BROWS = NMAT * TN;                 // weight rows per tile
+  constexpr int BPT = BROWS * 2 / kPT;             // 16-byte code chunks per thread (2 per row)
+  static_assert(BPT >= 1 && (BROWS * 2) % kPT == 0, "tile shape");
+  const int ar = tid / 4, aq = tid % 4;
+  const int64_t nbk = a.k / kBlock;
+  const int64_t rows0 = t.shared ? 0 : (int64_t)t.e * a.rows_per_expert;
+  const uint8_t* expm[2] = {(t.shared ? a.sexp0 : a.exp0) + rows0 * nbk,
+                            NMAT == 2 ? (t.shared ? a.sexp1 : a.exp1) + rows0 * nbk : nullptr};
+  const uint8_t* codem[2] = {(t.shared ? a.scode0 : a.code0) + rows0 * (a.k / 2),
+                             NMAT == 2 ? (t.shared ? a.scode1 : a.code1) + rows0 * (a.k / 2) : nullptr};
+
+  uint4 ra[2];
+  u32x4 rc[BPT];
+  uint32_t re[BPT];
+  auto load_step = [&](int k0) {
+    const int row = arow[ar];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[h] = make_uint4(0, 0, 0, 0);
+      if (row >= 0)
+        ra[h] = *reinterpret_cast<const uint4*>(a.a + (int64_t)row * a.lda + k0 + aq * 16 + h * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int idx = tid + i * kPT;               // 0 .. BROWS*2
+      const int br = idx / 2, half = idx % 2;
+      const int mat = br / TN, wr = br % TN;
+      const int64_t row = t.col0 + wr;
+      rc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codem[mat] + row * (a.k / 2) + k0 / 2) + half);
+      re[i] = *reinterpret_cast<const uint16_t*>(expm[mat] + row * nbk + k0 / 16 + 2 * half);
+    }
+  };
+  auto store_step = [&]() {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<uint4*>(&As[ar][aq * 16 + h * 8]) = permute8(ra[h]);
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int idx = tid + i * kPT;
+      const int br = idx / 2, half = idx % 2;
+      const int mat = br / TN, wr = br % TN;
+      uint32_t o[16];
+      dequant16(rc[i].x, rc[i].y, re[i] & 0xffu, o);
+      dequant16(rc[i].z, rc[i].w, re[i] >> 8, o + 8);
+      uint4* dst = reinterpret_cast<uint4*>(&Bs[mat][wr][half * 32]);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
+      dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
+    }
+  };
+
+  constexpr int NC = TN / 16;                      // 16-column subtiles per matrix
+  f32x4 acc[NMAT][NC];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_step(0);
+  for (int k0 = 0; k0 < a.k; k0 += kTK) {
+    __syncthreads();
+    store_step();
+    __syncthreads();
+    if (k0 + kTK < a.k) load_step(k0 + kTK);
+#pragma unroll
+    for (int ks = 0; ks < kTK / 32; ++ks) {
+      const int kk = ks * 32 + 8 * (lane / 16);
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[wave * 16 + (lane % 16)][kk]);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[m][c * 16 + (lane % 16)][kk]);
+          acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[m][c], 0, 0, 0);
+        }
+    }
+  }
+
+  // epilogue: lane holds rows wave*16 + 4*(lane/16) + i, column c*16 + lane%16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 16 + 4 * (lane / 16) + i;
+    if (t.row0 + r >= t.n) continue;
+    const int64_t pos = t.p0 + t.row0 + r;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = t.col0 + c * 16 + (lane % 16);
+      if constexpr (NMAT == 2) {
+        const float g = acc[0][c][i], u = acc[1][c][i];
+        const float hv = g / (1.0f + __expf(-g)) * u;
+        static_cast<uint16_t*>(a.c)[pos * a.ldc + col] = (uint16_t)f32_to_bf16_rne(hv);
+      } else {
+        static_cast<float*>(a.c)[pos * a.ldc + col] = acc[0][c][i];
+      }
+    }
+  }
+}
+
+// y[t] = sum_j w[t][j] * o[inv[t*K+j]] + g[t] * o[m*K + t]
+__global__ __launch_bounds__(256) void pf_combine_kernel(const float* o, const int32_t* inv, const float* w,
+                                                         const float* g, int m, int top_k, int hidden, float* y) {
+  const int t = blockIdx.y;
+  const int n4 = blockIdx.x * 256 + threadIdx.x;
+  if (n4 * 4 >= hidden) return;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < top_k; ++j) {
+    const float wj = w[(int64_t)t * top_k + j];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(o + (int64_t)inv[(int64_t)t * top_k + j] * hidden + n4 * 4);
+    acc.x = __builtin_fmaf(wj, v.x, acc.x);
+    acc.y = __builtin_fmaf(wj, v.y, acc.y);
+    acc.z = __builtin_fmaf(wj, v.z, acc.z);
+    acc.w = __builtin_fmaf(wj, v.w, acc.w);
+  }
+  if (g) {
+    const float gt = g[t];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(o + ((int64_t)m * top_k + t) * hidden + n4 * 4);
+    acc.x = __builtin_fmaf(gt, v.x, acc.x);
+    acc.y = __builtin_fmaf(gt, v.y, acc.y);
+    acc.z = __builtin_fmaf(gt, v.z, acc.z);
+    acc.w = __builtin_fmaf(gt, v.w, acc.w);
+  }
+  *reinterpret_cast<f32x4*>(y + (int64_t)t * hidden + n4 * 4) = acc;
+}
+
+constexpr int kTNGate = 64;      // columns per matrix in the gate/up tiles
+constexpr int kTNDown = 128;     // columns in the down tiles
+
+int grid_for(int m, int top_k, int n_exp, int shared, int nct) {
+  // upper bound of row tiles: every group may waste one partial tile
+  const int pairs = m * top_k + (shared ? m : 0);
+  const int groups = (n_exp < m * top_k ? n_exp : m * top_k) + (shared ? 1 : 0);
+  const int tiles = (pairs / kTM + groups) * nct;
+  return (tiles + 7) / 8 * 8;
+}
+
+}  // namespace
+
+size_t prefill_workspace_extra_bytes(int, int n_exp, int) { return (size_t)(n_exp + 2) * 4; }
+
+hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s) {
+  const bfp_moe_layer* L = p.L;
+  const int shared = L->sh_gate.fmt != 0;
+  const int H = (int)L->hidden, F = (int)L->inter, K = L->top_k;
+  if (F % kTNGate != 0 || H % kTNDown != 0 || H % kTK != 0 || F % kTK != 0) return hipErrorNotSupported;
+  const int32_t* tile_start = p.tile_start;
+  PfArgs a{};
+  a.active = p.active; a.n_active = p.n_active; a.offsets = p.offsets; a.perm = p.perm;
+  a.tile_start = tile_start; a.with_shared = shared; a.m = p.m; a.top_k = K;
+  // gate/up + SwiGLU -> h (bf16)
+  a.exp0 = L->gate.exp; a.code0 = L->gate.code; a.exp1 = L->up.exp; a.code1 = L->up.code;
+  if (shared) {
+    a.sexp0 = L->sh_gate.exp; a.scode0 = L->sh_gate.code; a.sexp1 = L->sh_up.exp; a.scode1 = L->sh_up.code;
+  }
+  a.rows_per_expert = F; a.k = H;
+  a.a = p.x; a.lda = H; a.a_by_token = 1;
+  a.c = p.h; a.ldc = F;
+  hipLaunchKernelGGL((grouped_gemm_kernel<kTNGate, 2>), dim3(grid_for(p.m, K, L->n_experts, shared, F / kTNGate)),
+                     dim3(kPT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // down -> o (fp32)
+  PfArgs b = a;
+  b.exp0 = L->down.exp; b.code0 = L->down.code; b.exp1 = nullptr; b.code1 = nullptr;
+  b.sexp0 = shared ? L->sh_down.exp : nullptr; b.scode0 = shared ? L->sh_down.code : nullptr;
+  b.sexp1 = nullptr; b.scode1 = nullptr;
+  b.rows_per_expert = H; b.k = F;
+  b.a = p.h; b.lda = F; b.a_by_token = 0;
+  b.c = p.o; b.ldc = H;
+  hipLaunchKernelGGL((grouped_gemm_kernel<kTNDown, 1>), dim3(grid_for(p.m, K, L->n_experts, shared, H / kTNDown)),
+                     dim3(kPT), 0, s, b);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  dim3 grid((H / 4 + 255) / 256, p.m);
+  hipLaunchKernelGGL(pf_combine_kernel, grid, dim3(256), 0, s, p.o, p.inv, p.w, p.g, p.m, K, H, p.y);
+  return hipGetLastError();
+}
+
+int prefill_tile_rows() { return kTM; }
 
 }  // namespace bfp

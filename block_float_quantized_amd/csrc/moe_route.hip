@@ -145,6 +145,14 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(DispatchArgs a) 
     }
     off[E] = s;
     if (a.n_active) *a.n_active = na;
+    if (a.tile_m > 0) {
+      // groups: the active experts in ascending order, then (optionally) the shared group
+      int ts = 0, g = 0;
+      for (int e = 0; e < E; ++e)
+        if (cnt[e] > 0) { a.tile_start[g++] = ts; ts += (cnt[e] + a.tile_m - 1) / a.tile_m; }
+      if (a.with_shared) { a.tile_start[g++] = ts; ts += (a.m + a.tile_m - 1) / a.tile_m; }
+      a.tile_start[g] = ts;
+    }
   }
   __syncthreads();
   if (tid < E) a.counts[tid] = cnt[tid];

@@ -105,3 +105,46 @@ def test_moe_decode_deterministic_and_row_invariant(moe_full):
     a = bfq.bfp_moe_forward(dev, x)
     b = bfq.bfp_moe_forward(dev, x)
     assert torch.equal(a, b)
+
+
+def _prefill_check(layer, dev, bank, x, bias, sample):
+    m = x.shape[0]
+    ids = torch.empty((m, 8), dtype=torch.int32, device="cuda")
+    y = bfq.bfp_moe_forward(dev, dev_bf16(x), topk_ids=ids).cpu().numpy()
+    rt_all = oracle.route(x, layer["router"], 8, bias=bias, sh_gate_bits=layer["sh_gate_w"])
+    assert np.array_equal(ids.cpu().numpy(), rt_all["ids"])
+    xs = x[sample]
+    rt = {k: v[sample] for k, v in rt_all.items()}
+    ref, norm = oracle.moe_prefill(bank, xs, rt)
+    return assert_within(y[sample], ref, norm, TOL, what=f"moe prefill m={m}")
+
+
+def test_moe_prefill_small(moe_full):
+    layer, dev, bank = moe_full
+    note("moe prefill m=40")
+    x = synth.moe_tokens(40, 7)
+    _prefill_check(layer, dev, bank, x, None, np.arange(40))
+
+
+def test_moe_prefill_chunk_2048(moe_full):
+    """The 2,048-token prefill chunk with a skewed N(0, 1.5) per-expert router bias."""
+    layer, dev, bank = moe_full
+    note("moe prefill m=2048 with bias")
+    bias = synth.router_bias(0)
+    devb = bfq.MoeLayer(**{**dev.__dict__, "router_bias": dev_f32(bias)})
+    x = synth.moe_tokens(2048, 0, cfg_id=5)
+    sample = np.unique(np.concatenate([[0, 2047], np.random.default_rng(5).integers(0, 2048, 62)]))
+    _prefill_check(layer, devb, bank, x, bias, sample)
+
+
+def test_moe_prefill_and_decode_agree(moe_full):
+    """The same 33 tokens through the prefill path and through 33 single-token decodes:
+    identical routing, outputs equal up to the bf16 rounding of h in prefill."""
+    layer, dev, bank = moe_full
+    note("moe prefill vs decode")
+    x = synth.moe_tokens(33, 11)
+    yp = bfq.bfp_moe_forward(dev, dev_bf16(x)).cpu().numpy()
+    yd = np.concatenate([bfq.bfp_moe_forward(dev, dev_bf16(x[i:i + 1])).cpu().numpy() for i in range(33)])
+    rt = oracle.route(x, layer["router"], 8, sh_gate_bits=layer["sh_gate_w"])
+    _, norm = oracle.moe_decode(bank, x, rt)
+    assert np.all(np.abs(yp - yd) <= 2.0 ** -7 * norm)
