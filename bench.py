@@ -1,19 +1,24 @@
 """Benchmark of the BFP4/BFP8 weight-streaming matmul path on one MI355X.
 
-One step = one decode pass of the dense BFP4 MLP at 27B-class shapes: x is M x 5120 bf16;
-gate and up (5120 -> 17408, BFP4) run as one streamed GEMV with a fused SwiGLU epilogue,
-then the BFP4 down projection (17408 -> 5120) writes bf16 y. Weights are seeded synthetic
-N(0, 0.02) x per-row LogNormal(0, 0.5), quantized on the GPU before timing.
+Headline step: one decode pass of the dense BFP4 MLP at 27B-class shapes. x is M x 5120
+bf16; gate and up (5120 -> 17408, BFP4) run as one streamed GEMV with a fused SwiGLU
+epilogue (h kept in fp32), then the BFP4 down projection (17408 -> 5120) writes bf16 y.
 
-Protocol: the packed weights are replicated so that consecutive steps read different copies
-(>= 1 GiB rotation, more than four times the 256 MB last-level cache), so the numbers are
-HBM numbers. W warm-up steps, then K timed steps between two events on the launch stream.
-The headline value is algorithmic bytes (packed weights + x + y) per step divided by the
-step time. The dominant kernel (gate/up + SwiGLU) is also timed launch by launch with events
-on the same stream for the roofline entry. The CPU oracle is timed on a bounded sample of
-the same work on the host.
+The same run also measures the other workloads of the path (one entry each under
+"workloads"): the single BFP8 GEMV 2048 x 2048, the dense MLP at M = 8 / 16 / 32, the BFP8
+fused QKV / output projections and the 151,936-row LM head at M = 1 and 16, the 256-expert
+top-8 BFP4 MoE layer at decode (M = 1 / 8 / 16) and the 2,048-token MoE prefill chunk.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--M 1] [--sweep]
+Protocol: inputs are seeded synthetic tensors (the `synth` module), quantized on the GPU
+before timing. Packed weights are replicated (or several layers are built) so consecutive
+calls read different copies, >= 1 GiB apart in total (more than four times the 256 MB
+last-level cache): the bandwidths are HBM numbers. Each timed loop runs W warm-up calls, then
+K calls between two events on the launch stream. Bandwidth = algorithmic bytes (packed
+weights actually read + activations in + outputs out) / time per call. The dominant kernel
+of the headline step (gate/up + SwiGLU GEMV) is timed alone over K back-to-back launches for
+the roofline entry. The CPU oracle is timed on a bounded sample of the headline step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--M 1] [--quick]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -31,170 +36,288 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "achieved HBM GB/s (% of peak) + µs/call, BFP4/BFP8 GEMV & MoE at M=1..32"
 HIDDEN, INTER = 5120, 17408
+MIN_ROTATION = 1 << 30
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--M", type=int, default=1)
-    ap.add_argument("--replicas", type=int, default=8)
-    ap.add_argument("--sweep", action="store_true", help="also time M = 1, 8, 16, 32")
+    ap.add_argument("--quick", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="rows per matrix in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows per matrix in the CPU sample")
     return ap.parse_args()
 
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def bf16_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def replicas_for(nbytes: int, cap: int = 512) -> int:
+    return int(min(cap, max(2, -(-MIN_ROTATION // max(nbytes, 1)))))
+
+
+def clone(m):
+    import block_float_quantized_amd as bfq
+    return bfq.BfpMatrix(m.fmt, m.n, m.k, m.exp.clone(), m.code.clone())
+
+
+def quantize(fmt, w):
+    import torch
+    import block_float_quantized_amd as bfq
+    t = torch.from_numpy(w).to("cuda")
+    m = bfq.bfp_quantize(fmt, t)
+    del t
+    return m
+
+
+def timed(fn, steps, warmup):
+    """Average ms per call of fn(i) over `steps` calls after `warmup` calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        fn(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+# ---- headline: dense BFP4 MLP decode ------------------------------------------------------
 
 def mlp_bytes(m: int) -> dict:
     import block_float_quantized_amd as bfq
     w_gu = bfq.exp_bytes(INTER, HIDDEN) + bfq.code_bytes(4, INTER, HIDDEN)
     w_d = bfq.exp_bytes(HIDDEN, INTER) + bfq.code_bytes(4, HIDDEN, INTER)
     return {
-        "weights": 2 * w_gu + w_d,
-        "gateup_kernel": 2 * w_gu + m * HIDDEN * 2 + m * INTER * 4,   # weights + x + h written
+        "gateup_kernel": 2 * w_gu + m * HIDDEN * 2 + m * INTER * 4,   # weights + x in + h out
         "step": 2 * w_gu + w_d + m * HIDDEN * 2 + m * HIDDEN * 2,     # weights + x in + y out
     }
 
 
-def run_gpu(args, m: int, mats, x):
-    import torch
-    import block_float_quantized_amd as bfq
-    stream = torch.cuda.current_stream()
-    R = len(mats)
-    h = torch.empty((m, INTER), dtype=torch.float32, device="cuda")
-    y = torch.empty((m, HIDDEN), dtype=torch.bfloat16, device="cuda")
-
-    def step(i, ev=None):
-        g, u, d = mats[i % R]
-        if ev is not None:
-            ev[0].record(stream)
-        bfq.bfp_gemm(g, x, w_up=u, out=h, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        bfq.bfp_gemm(d, h, out_dtype=torch.bfloat16, out=y, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # whole-step timing
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    # per-launch timing of the dominant kernel (events around each gate/up launch)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    return ms_step, gu_ms
-
-
-def make_weights(replicas: int, seed: int = 0):
-    import torch
-    import block_float_quantized_amd as bfq
+def make_mlp(replicas: int, seed: int = 0):
     import synth
     c = synth.mlp_case(1, seed)
-    base = []
-    for name in ("wg", "wu", "wd"):
-        w = torch.from_numpy(c[name]).to("cuda")
-        base.append(bfq.bfp_quantize(4, w))
-        del w
-    mats = [tuple(base)]
-    for _ in range(replicas - 1):
-        mats.append(tuple(bfq.BfpMatrix(b.fmt, b.n, b.k, b.exp.clone(), b.code.clone()) for b in base))
+    base = tuple(quantize(4, c[name]) for name in ("wg", "wu", "wd"))
+    mats = [base] + [tuple(clone(b) for b in base) for _ in range(replicas - 1)]
     return c, mats
 
 
+def run_mlp(args, m, mats, xb):
+    import torch
+    import block_float_quantized_amd as bfq
+    x = bf16_dev(xb)
+    h = torch.empty((m, INTER), dtype=torch.float32, device="cuda")
+    y = torch.empty((m, HIDDEN), dtype=torch.bfloat16, device="cuda")
+    R = len(mats)
+
+    def step(i):
+        g, u, d = mats[i % R]
+        bfq.bfp_gemm(g, x, w_up=u, out=h)
+        bfq.bfp_gemm(d, h, out_dtype=torch.bfloat16, out=y)
+
+    def gateup(i):
+        g, u, _ = mats[i % R]
+        bfq.bfp_gemm(g, x, w_up=u, out=h)
+
+    ms_step = timed(step, args.steps, args.warmup)
+    ms_gu = timed(gateup, args.steps, args.warmup)
+    b = mlp_bytes(m)
+    return {"us_per_call": ms_step * 1e3, "GB/s": b["step"] / (ms_step * 1e-3) / 1e9,
+            "gateup_us": ms_gu * 1e3, "gateup_GB/s": b["gateup_kernel"] / (ms_gu * 1e-3) / 1e9,
+            "bytes": b["step"], "tok_per_s": m / (ms_step * 1e-3)}
+
+
 def cpu_baseline(c: dict, rows: int, xbits: np.ndarray) -> dict:
-    """Time the CPU oracle (decode the packed bytes, fp64 GEMV) on `rows` rows of each matrix."""
+    """Time the CPU oracle (decode the packed bytes, fp64 GEMV, SwiGLU) on `rows` rows of each
+    matrix of the headline step, one thread."""
     import oracle
     from threadpoolctl import threadpool_limits
     m = xbits.shape[0]
     x = oracle.bf16_to_f64(xbits)
-    packed = {}
-    for name in ("wg", "wu", "wd"):
-        w = c[name][:rows]
-        packed[name] = (oracle.encode(w, 4), w.shape)
+    packed = {name: (oracle.encode(c[name][:rows], 4), c[name][:rows].shape) for name in ("wg", "wu", "wd")}
     nbytes = sum(e.nbytes + cc.nbytes for (e, cc), _ in packed.values())
     with threadpool_limits(limits=1):
         t = time.perf_counter()
         (eg, cg), (n, k) = packed["wg"]
         (eu, cu), _ = packed["wu"]
-        g = oracle.gemm(x, oracle.decode(eg, cg, 4, n, k))
-        u = oracle.gemm(x, oracle.decode(eu, cu, 4, n, k))
-        hh = oracle.swiglu(g, u)
+        hh = oracle.swiglu(oracle.gemm(x, oracle.decode(eg, cg, 4, n, k)), oracle.gemm(x, oracle.decode(eu, cu, 4, n, k)))
         (ed, cd), (nd, kd) = packed["wd"]
         hfull = np.zeros((m, kd))
         hfull[:, :hh.shape[1]] = hh
         oracle.gemm(hfull, oracle.decode(ed, cd, 4, nd, kd))
         dt = time.perf_counter() - t
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} rows of each of gate, up and down (M={m}): decode packed BFP4 + fp64 GEMV, "
-                      f"{nbytes / 1e6:.1f} MB of packed weights in {dt:.2f} s, 1 thread"}
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} rows of gate, up and down at M={m}: decode packed BFP4 + fp64 GEMV + "
+                      f"SwiGLU, {nbytes / 1e6:.1f} MB of packed weights in {dt:.2f} s on 1 thread"}
+
+
+# ---- other workloads -----------------------------------------------------------------------
+
+def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32"):
+    """Time bfp_gemm on one matrix over cold replicas for each x in xs_bits (dict M -> bits)."""
+    import torch
+    import block_float_quantized_amd as bfq
+    base = quantize(fmt, w)
+    R = replicas_for(base.nbytes)
+    mats = [base] + [clone(base) for _ in range(R - 1)]
+    out = {}
+    for m, xb in xs_bits.items():
+        x = bf16_dev(xb)
+        y = torch.empty((m, base.n), dtype=torch.float32, device="cuda")
+        ms = timed(lambda i: bfq.bfp_gemm(mats[i % R], x, out=y), args.steps, args.warmup)
+        nbytes = base.nbytes + m * base.k * 2 + m * base.n * 4
+        out[f"{name} M={m}"] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                                "bytes": nbytes, "replicas": R, "tok_per_s": round(m / (ms * 1e-3), 1)}
+        log(f"{name} M={m}: {ms * 1e3:.2f} us")
+    del mats
+    torch.cuda.empty_cache()
+    return out
+
+
+def moe_workloads(args):
+    import torch
+    import block_float_quantized_amd as bfq
+    import synth
+    out = {}
+    layer = synth.moe_layer(0)
+    log("MoE layer drawn")
+    q = {k: quantize(4, layer[k]) for k in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")}
+    expert_bytes = (q["gate"].nbytes + q["up"].nbytes + q["down"].nbytes) // layer["n_experts"]
+    shared_bytes = q["sh_gate"].nbytes + q["sh_up"].nbytes + q["sh_down"].nbytes
+    router_bytes = layer["router"].nbytes + layer["sh_gate_w"].nbytes
+    nl = 4
+    layers = []
+    for r in range(nl):
+        qq = q if r == 0 else {k: clone(v) for k, v in q.items()}
+        layers.append(bfq.MoeLayer(256, 8, 2048, 512, bf16_dev(layer["router"]), None, qq["gate"], qq["up"],
+                                   qq["down"], qq["sh_gate"], qq["sh_up"], qq["sh_down"],
+                                   bf16_dev(layer["sh_gate_w"])))
+    del layer
+    for m in (1, 8, 16):
+        xs = [bf16_dev(synth.moe_tokens(m, s)) for s in range(8)]
+        ws = torch.empty((bfq.bfp_moe_workspace_bytes(layers[0], m),), dtype=torch.uint8, device="cuda")
+        y = torch.empty((m, 2048), dtype=torch.float32, device="cuda")
+        ids = torch.empty((m, 8), dtype=torch.int32, device="cuda")
+        distinct = []
+        for s in range(8):
+            bfq.bfp_moe_forward(layers[0], xs[s], out=y, workspace=ws, topk_ids=ids)
+            distinct.append(len(np.unique(ids.cpu().numpy())))
+        ms = timed(lambda i: bfq.bfp_moe_forward(layers[i % nl], xs[i % 8], out=y, workspace=ws),
+                   args.steps, args.warmup)
+        d = float(np.mean(distinct))
+        nbytes = d * expert_bytes + shared_bytes + router_bytes + m * 2048 * 2 + m * 2048 * 4
+        out[f"moe decode M={m}"] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                    "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                                    "distinct_experts": d, "bytes": int(nbytes),
+                                    "tok_per_s": round(m / (ms * 1e-3), 1)}
+        log(f"moe decode M={m}: {ms * 1e3:.2f} us, {d:.1f} experts")
+    # prefill chunk: 2,048 tokens with the skewed router bias
+    bias = torch.from_numpy(synth.router_bias(0)).to("cuda")
+    for L in layers:
+        L.router_bias = bias
+    m = 2048
+    xs = [bf16_dev(synth.moe_tokens(m, s, cfg_id=5)) for s in range(2)]
+    ws = torch.empty((bfq.bfp_moe_workspace_bytes(layers[0], m),), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, 2048), dtype=torch.float32, device="cuda")
+    ids = torch.empty((m, 8), dtype=torch.int32, device="cuda")
+    bfq.bfp_moe_forward(layers[0], xs[0], out=y, workspace=ws, topk_ids=ids)
+    used = len(np.unique(ids.cpu().numpy()))
+    steps = max(10, args.steps // 10)
+    ms = timed(lambda i: bfq.bfp_moe_forward(layers[i % nl], xs[i % 2], out=y, workspace=ws), steps, 3)
+    flops = 2.0 * (m * 8 + m) * 3 * 2048 * 512
+    router_flops = 2.0 * m * 257 * 2048
+    tfs = flops / (ms * 1e-3) / 1e12
+    out["moe prefill M=2048"] = {"us_per_call": round(ms * 1e3, 1), "TFLOP/s": round(tfs, 1),
+                                 "pct_bf16_mfma_peak": round(100 * tfs / BF16_MFMA_PEAK_TFLOPS, 1),
+                                 "expert_GFLOP": round(flops / 1e9, 2), "router_GFLOP": round(router_flops / 1e9, 2),
+                                 "experts_used": used, "tok_per_s": round(m / (ms * 1e-3), 1)}
+    log(f"moe prefill: {ms * 1e3:.1f} us, {tfs:.1f} TFLOP/s, {used} experts used")
+    del layers
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}), flush=True)
         sys.exit(2)
     import torch
     import block_float_quantized_amd as bfq
+    import synth
     bfq.lib()
     torch.cuda.set_device(0)
-    import synth
-    c, mats = make_weights(args.replicas)
-    Ms = [args.M] + ([mm for mm in (1, 8, 16, 32) if mm != args.M] if args.sweep else [])
-    results = {}
-    for m in Ms:
-        xb = synth.mlp_case(m, 0)["x"] if m != 1 else c["x"]
-        x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).to("cuda").view(torch.bfloat16)
-        ms_step, gu_ms = run_gpu(args, m, mats, x)
-        b = mlp_bytes(m)
-        results[m] = {
-            "ms_per_step": ms_step,
-            "gbs": b["step"] / (ms_step * 1e-3) / 1e9,
-            "gateup_us": gu_ms * 1e3,
-            "gateup_gbs": b["gateup_kernel"] / (gu_ms * 1e-3) / 1e9,
-            "step_bytes": b["step"],
-        }
-    r = results[args.M]
+    c, mats = make_mlp(8)
+    log("MLP weights quantized")
+    xb = synth.mlp_case(args.M, 0)["x"] if args.M != 1 else c["x"]
+    head = run_mlp(args, args.M, mats, xb)
+    log(f"MLP M={args.M}: {head['us_per_call']:.2f} us")
+    workloads = {f"dense BFP4 MLP M={args.M}": {k: round(v, 2) for k, v in head.items()}}
+    if not args.quick:
+        for m in (1, 8, 16, 32):
+            if m == args.M:
+                continue
+            r = run_mlp(args, m, mats, synth.mlp_case(m, 0)["x"])
+            workloads[f"dense BFP4 MLP M={m}"] = {k: round(v, 2) for k, v in r.items()}
+            log(f"MLP M={m}: {r['us_per_call']:.2f} us")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(c, args.cpu_rows, xb)
+    del mats, c
+    torch.cuda.empty_cache()
+    if not args.quick:
+        g = synth.gemv_case(0)
+        workloads.update(gemv_workload(args, "BFP8 GEMV 2048x2048", g["w"], 8, {1: g["x"]}))
+        p1, p16 = synth.proj_case(1, 0, with_lm=False), synth.proj_case(16, 0, with_lm=False)
+        workloads.update(gemv_workload(args, "BFP8 QKV 2048->5120", p1["wqkv"], 8, {1: p1["x"], 16: p16["x"]}))
+        workloads.update(gemv_workload(args, "BFP8 O 4096->2048", p1["wo"], 8, {1: p1["xo"], 16: p16["xo"]}))
+        del p1, p16
+        lm = synth.dense_weights(0, 3, "lm", 151936, 2048, 0.02)
+        workloads.update(gemv_workload(args, "BFP8 LM head 2048->151936", lm,
+                                       8, {1: synth.proj_case(1, 0, with_lm=False)["x"],
+                                           16: synth.proj_case(16, 0, with_lm=False)["x"]}))
+        del lm
+        workloads.update(moe_workloads(args))
     line = {
         "metric": METRIC,
-        "value": round(r["gbs"], 1),
+        "value": round(head["GB/s"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["ms_per_step"], 5),
-        "us_per_call": round(r["ms_per_step"] * 1e3, 2),
-        "pct_hbm_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 1),
+        "ms_per_step": round(head["us_per_call"] * 1e-3, 5),
+        "us_per_call": round(head["us_per_call"], 2),
+        "pct_hbm_peak": round(100 * head["GB/s"] / HBM_PEAK_GBS, 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"dense BFP4 MLP decode, 27B-class: x {args.M}x5120 bf16, gate/up 5120x17408 "
-                               f"BFP4 + SwiGLU, down 17408x5120 BFP4, bf16 out",
-                   "M": args.M, "replicas": args.replicas, "bytes_per_step": r["step_bytes"]},
-        "roofline": {"bound": "hbm", "achieved": round(r["gateup_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(r["gateup_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_kernel<BFP4, SwiGLU> (gate+up)", "avg_us": round(r["gateup_us"], 2)},
+                               f"BFP4 + SwiGLU (fp32 h), down 17408x5120 BFP4, bf16 out",
+                   "M": args.M, "replicas": 8, "bytes_per_step": head["bytes"]},
+        "roofline": {"bound": "hbm", "achieved": round(head["gateup_GB/s"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head["gateup_GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_kernel BFP4 gate+up+SwiGLU", "avg_us": round(head["gateup_us"], 2)},
+        "workloads": workloads,
     }
-    if args.sweep:
-        line["by_M"] = {str(m): {"us_per_call": round(v["ms_per_step"] * 1e3, 2), "GB/s": round(v["gbs"], 1),
-                                 "tok_per_s": round(m / (v["ms_per_step"] * 1e-3), 1)} for m, v in results.items()}
-    if not args.no_cpu_baseline:
-        xb = synth.mlp_case(args.M, 0)["x"] if args.M != 1 else c["x"]
-        line["cpu_baseline"] = cpu_baseline(c, args.cpu_rows, xb)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
