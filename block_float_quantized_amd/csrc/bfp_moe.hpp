@@ -19,6 +19,8 @@ struct RouteArgs {
   float* w;                    // [m][top_k]
   float* g;                    // [m] or null
 };
+// Bytes of the logits workspace region for m tokens (shared by both routing methods).
+size_t route_workspace_bytes(int m, int n_exp);
 hipError_t router_launch(const RouteArgs& a, hipStream_t s);
 
 struct DispatchArgs {

@@ -61,7 +61,7 @@ Layout layout(const bfp_moe_layer* L, int64_t m, bool with_experts) {
   const int64_t E = L->n_experts, K = L->top_k, H = L->hidden, F = L->inter;
   const int64_t pairs = m * K + m;
   const bool prefill = m > BFP_GEMM_MAX_M;
-  y.logits = place(off, (size_t)m * (E + 1) * sizeof(double));
+  y.logits = place(off, bfp::route_workspace_bytes((int)m, (int)E));
   if (with_experts) {
     y.ids = place(off, (size_t)m * K * 4);
     y.w = place(off, (size_t)m * K * 4);

@@ -22,11 +22,15 @@ inline __host__ __device__ int mb_bucket(int n) {
   return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : 32;
 }
 
+// rows per lane group (one: these calls are short and latency-bound, so more workgroups win)
+template <int NMAT> constexpr int moe_rt() { return 1; }
+
 template <int NMAT, bool XB, int MB, int LPR>
 __device__ __forceinline__ void run_tile(const GemvArgs& a, int row_base, const int* xrow, const int* yrow,
                                          uint32_t* xs) {
   constexpr int U = MB <= 4 ? 2 : 1;
-  gemv_tile<4, MB, 1, LPR, NMAT, U, 2, XB, kMoeThreads>(a, row_base, xrow, yrow, xs);
+  constexpr int RT = MB <= 8 ? moe_rt<NMAT>() : 1;
+  gemv_tile<4, MB, RT, LPR, NMAT, U, 2, XB, kMoeThreads>(a, row_base, xrow, yrow, xs);
 }
 
 template <int NMAT, bool XB, int MBMAX, int LPR>
@@ -62,8 +66,9 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemv_kernel(MoeGemvArgs ma, i
   a.x = ma.x; a.ldx = ma.ldx;
   a.y = ma.y; a.ldy = ma.ldy; a.y_bf16 = ma.y_bf16;
   a.n = ma.rows_per_expert; a.k = ma.k; a.m = n; a.kc = kc;
-  constexpr int RPW = (kMoeThreads / kWave) * (kWave / LPR);
-  const int row_base = blockIdx.x * RPW;
+  const int rpw = (kMoeThreads / kWave) * (kWave / LPR) * (mb_bucket(n) <= 8 ? moe_rt<NMAT>() : 1);
+  const int row_base = blockIdx.x * rpw;
+  if (row_base >= ma.rows_per_expert) return;
   // xrow/yrow are read after the first barrier inside the tile
   switch (mb_bucket(n)) {
     case 1: run_tile<NMAT, XB, 1, LPR>(a, row_base, xrow, yrow, xs); break;
@@ -81,6 +86,8 @@ hipError_t launch_mbmax(const MoeGemvArgs& ma, hipStream_t s) {
   using L = XLayout<XB, 32>;
   const int kc = pick_kc(ma.k, MBMAX, 32, LPR, L::kBytesPerValue);
   const size_t lds = (size_t)MBMAX * (kc / 32) * L::kStrideDw * sizeof(uint32_t);
+  // enough row tiles for the smallest rows-per-workgroup a group can pick (RT = 1 when
+  // more than 8 pairs share an expert); workgroups past the end of a group exit
   constexpr int RPW = (kMoeThreads / kWave) * (kWave / LPR);
   const int groups = (ma.m * ma.top_k < 256 ? ma.m * ma.top_k : 256) + (ma.scode0 ? 1 : 0);
   dim3 grid((ma.rows_per_expert + RPW - 1) / RPW, groups);

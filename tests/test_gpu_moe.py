@@ -148,3 +148,20 @@ def test_moe_prefill_and_decode_agree(moe_full):
     rt = oracle.route(x, layer["router"], 8, sh_gate_bits=layer["sh_gate_w"])
     _, norm = oracle.moe_decode(bank, x, rt)
     assert np.all(np.abs(yp - yd) <= 2.0 ** -7 * norm)
+
+
+def test_route_many_tokens_with_exact_ties():
+    """Many-token routing (certified matrix-core logits + exact re-check) with planted exact
+    ties: duplicated router rows must rank by expert index, as the oracle does."""
+    note("route m=300 with duplicated router rows")
+    router, shg = synth.moe_router(3)
+    for a, b in ((5, 17), (40, 41), (100, 200), (7, 255)):
+        router[b] = router[a]
+    lay, _, _ = _router_only_layer(3)
+    lay.router_w = dev_bf16(router)
+    x = synth.moe_tokens(300, 3)
+    ids, w, g = bfq.bfp_moe_route(lay, dev_bf16(x))
+    ref = oracle.route(x, router, 8, sh_gate_bits=shg)
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+    assert np.allclose(w.cpu().numpy(), ref["r"], rtol=1e-6, atol=0)
+    assert np.allclose(g.cpu().numpy(), ref["g"], rtol=1e-6, atol=0)
