@@ -15,9 +15,11 @@
 //    takes a contiguous range of tiles, ordered (group, column tile, row tile): the tiles
 //    that reuse one expert's weights share an L2.
 //  * Per K step of 64: the activation rows are gathered (token rows of x, or pair rows of h)
-//    and the BFP4 weight rows are dequantized to bf16 in registers and stored in LDS; the
-//    next step's global loads are issued before the current step's MFMAs.
-//  * v_mfma_f32_16x16x32_bf16 with fp32 accumulation; each wave owns 16 rows of the tile.
+//    into LDS; each lane loads and dequantizes its own weight values straight into MFMA B
+//    operands (the weights never go through LDS); the next step's global loads are issued
+//    before the current step's MFMAs.
+//  * v_mfma_f32_32x32x16_bf16 with fp32 accumulation; each wave owns all 64 rows of the tile
+//    and 64 output columns.
 //    A and B share one permutation of K inside every 8-value group (the order the BFP4
 //    unpack produces pairs in), which leaves every dot product unchanged.
 //  * Dequantization is exact: a nibble becomes an FP8 E4M3 subnormal (mag * 2^-9) and the
@@ -146,18 +148,30 @@ __device__ __forceinline__ bool find_tile(const PfArgs& a, TileInfo& t) {
   return true;
 }
 
-// Grouped GEMM C[pos][col] = A[row(pos)] . W_e[col] for one tile, NMAT weight matrices of TN
-// rows each. NMAT = 2: SwiGLU of the two (gate, up), stored as bf16; NMAT = 1: fp32 store.
-template <int TN, int NMAT>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Grouped GEMM C[pos][col] = A[row(pos)] . W_e[col] for one tile of kTM rows, on
+// v_mfma_f32_32x32x16_bf16. Each of the 4 waves owns all kTM rows (two 32-row A fragments)
+// and NB = 2 B tiles of 32 columns: NMAT = 2 -> the same 32 columns of gate and of up (the
+// SwiGLU pair lands in one lane), NMAT = 1 -> 64 adjacent columns. A workgroup therefore
+// covers TN = 4 * 32 * 2 / NMAT columns of each matrix.
+//
+// Per K step of 64: the gathered A rows go through LDS (shared by the 4 waves); every lane
+// loads the 16 code bytes (32 values) of each of its B rows directly and dequantizes them
+// in registers, so the weights never touch LDS. Lane group g = lane / 32 takes K values
+// [32g, 32g + 32) of the step, 8 per MFMA; its A fragment reads the same K values from LDS.
+template <int NMAT>
 __global__ __launch_bounds__(kPT) void grouped_gemm_kernel(PfArgs a) {
-  __shared__ __align__(16) uint16_t As[kTM][kLDK];
-  __shared__ __align__(16) uint16_t Bs[NMAT][TN][kLDK];
+  constexpr int NB = 2;                            // 32-column B tiles per wave
+  constexpr int TN = 4 * 32 * NB / NMAT;           // columns per matrix per workgroup
+  __shared__ __align__(16) uint16_t As[2][kTM][kLDK];
   __shared__ int arow[kTM];
   TileInfo t;
   if (!find_tile<TN>(a, t)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane / 32, lc = lane % 32;
   if (tid < kTM) {
     const int r = t.row0 + tid;
     int row = -1;
@@ -170,106 +184,112 @@ __global__ __launch_bounds__(kPT) void grouped_gemm_kernel(PfArgs a) {
   }
   __syncthreads();
 
-  // this thread's share of the global loads of one K step
-  //  A: 64 rows x 64 bf16 = 256 x 32 B: row tid/4, 16 values at (tid%4)*16
-  //  B: NMAT x TN rows x 64 values of BFP4 = 32 B per row: row (tid*?) ...
-  constexpr int BROWS = NMAT * TN;                 // weight rows per tile
-  constexpr int BPT = BROWS * 2 / kPT;             // 16-byte code chunks per thread (2 per row)
-  static_assert(BPT >= 1 && (BROWS * 2) % kPT == 0, "tile shape");
-  const int ar = tid / 4, aq = tid % 4;
   const int64_t nbk = a.k / kBlock;
   const int64_t rows0 = t.shared ? 0 : (int64_t)t.e * a.rows_per_expert;
-  const uint8_t* expm[2] = {(t.shared ? a.sexp0 : a.exp0) + rows0 * nbk,
+  const uint8_t* expb[2] = {(t.shared ? a.sexp0 : a.exp0) + rows0 * nbk,
                             NMAT == 2 ? (t.shared ? a.sexp1 : a.exp1) + rows0 * nbk : nullptr};
-  const uint8_t* codem[2] = {(t.shared ? a.scode0 : a.code0) + rows0 * (a.k / 2),
+  const uint8_t* codeb[2] = {(t.shared ? a.scode0 : a.code0) + rows0 * (a.k / 2),
                              NMAT == 2 ? (t.shared ? a.scode1 : a.code1) + rows0 * (a.k / 2) : nullptr};
+  // B row (output column) of tile b of this lane, and the matrix it belongs to
+  const uint8_t* bcode[NB];
+  const uint8_t* bexp[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int mat = NMAT == 2 ? b : 0;
+    const int col = NMAT == 2 ? t.col0 + wave * 32 + lc : t.col0 + wave * 64 + b * 32 + lc;
+    bcode[b] = codeb[mat] + (int64_t)col * (a.k / 2);
+    bexp[b] = expb[mat] + (int64_t)col * nbk;
+  }
+  // A staging: 64 rows x 64 values = 256 threads x 16 values
+  const int ar = tid / 4, aq = tid % 4;
+  const int arow_this = arow[ar];
 
-  uint4 ra[2];
-  u32x4 rc[BPT];
-  uint32_t re[BPT];
-  auto load_step = [&](int k0) {
-    const int row = arow[ar];
+  // global loads of one K step, kept in registers until the step is consumed
+  struct StepRegs {
+    uint4 ra[2];
+    u32x4 rc[NB];
+    uint32_t re[NB];
+  };
+  auto load_step = [&](StepRegs& R, int k0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      ra[h] = make_uint4(0, 0, 0, 0);
-      if (row >= 0)
-        ra[h] = *reinterpret_cast<const uint4*>(a.a + (int64_t)row * a.lda + k0 + aq * 16 + h * 8);
+      R.ra[h] = make_uint4(0, 0, 0, 0);
+      if (arow_this >= 0)
+        R.ra[h] = *reinterpret_cast<const uint4*>(a.a + (int64_t)arow_this * a.lda + k0 + aq * 16 + h * 8);
     }
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int idx = tid + i * kPT;               // 0 .. BROWS*2
-      const int br = idx / 2, half = idx % 2;
-      const int mat = br / TN, wr = br % TN;
-      const int64_t row = t.col0 + wr;
-      rc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codem[mat] + row * (a.k / 2) + k0 / 2) + half);
-      re[i] = *reinterpret_cast<const uint16_t*>(expm[mat] + row * nbk + k0 / 16 + 2 * half);
-    }
-  };
-  auto store_step = [&]() {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<uint4*>(&As[ar][aq * 16 + h * 8]) = permute8(ra[h]);
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int idx = tid + i * kPT;
-      const int br = idx / 2, half = idx % 2;
-      const int mat = br / TN, wr = br % TN;
-      uint32_t o[16];
-      dequant16(rc[i].x, rc[i].y, re[i] & 0xffu, o);
-      dequant16(rc[i].z, rc[i].w, re[i] >> 8, o + 8);
-      uint4* dst = reinterpret_cast<uint4*>(&Bs[mat][wr][half * 32]);
-      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
-      dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
+    for (int b = 0; b < NB; ++b) {
+      R.rc[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bcode[b] + (k0 + 32 * g) / 2));
+      R.re[b] = *reinterpret_cast<const uint16_t*>(bexp[b] + (k0 + 32 * g) / 16);
     }
   };
 
-  constexpr int NC = TN / 16;                      // 16-column subtiles per matrix
-  f32x4 acc[NMAT][NC];
+  f32x16 acc[2][NB];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b) acc[rt][b] = f32x16{};
 
-  load_step(0);
-  for (int k0 = 0; k0 < a.k; k0 += kTK) {
-    __syncthreads();
-    store_step();
-    __syncthreads();
-    if (k0 + kTK < a.k) load_step(k0 + kTK);
+  // consume one step: dequantize B, stage A into LDS buffer `buf`, one barrier, MFMAs; the
+  // registers of the step are free again once the barrier is passed, so the load of the
+  // step two ahead is issued before the MFMAs
+  auto consume = [&](StepRegs& R, int buf, int k_next2) {
+    uint32_t dq[NB][16];
 #pragma unroll
-    for (int ks = 0; ks < kTK / 32; ++ks) {
-      const int kk = ks * 32 + 8 * (lane / 16);
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[wave * 16 + (lane % 16)][kk]);
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&Bs[m][c * 16 + (lane % 16)][kk]);
-          acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[m][c], 0, 0, 0);
-        }
+    for (int b = 0; b < NB; ++b) {
+      dequant16(R.rc[b].x, R.rc[b].y, R.re[b] & 0xffu, dq[b]);
+      dequant16(R.rc[b].z, R.rc[b].w, R.re[b] >> 8, dq[b] + 8);
     }
-  }
-
-  // epilogue: lane holds rows wave*16 + 4*(lane/16) + i, column c*16 + lane%16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 16 + 4 * (lane / 16) + i;
-    if (t.row0 + r >= t.n) continue;
-    const int64_t pos = t.p0 + t.row0 + r;
+    for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(&As[buf][ar][aq * 16 + h * 8]) = permute8(R.ra[h]);
+    __syncthreads();
+    if (k_next2 < a.k) load_step(R, k_next2);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int col = t.col0 + c * 16 + (lane % 16);
-      if constexpr (NMAT == 2) {
-        const float g = acc[0][c][i], u = acc[1][c][i];
-        const float hv = g / (1.0f + __expf(-g)) * u;
-        static_cast<uint16_t*>(a.c)[pos * a.ldc + col] = (uint16_t)f32_to_bf16_rne(hv);
-      } else {
-        static_cast<float*>(a.c)[pos * a.ldc + col] = acc[0][c][i];
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 bf[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x4 v = u32x4{dq[b][4 * st], dq[b][4 * st + 1], dq[b][4 * st + 2], dq[b][4 * st + 3]};
+        bf[b] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[buf][rt * 32 + lc][32 * g + 8 * st]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[rt][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[b], acc[rt][b], 0, 0, 0);
       }
     }
+  };
+
+  // two register sets, two LDS buffers: step s uses set s % 2 and buffer s % 2. Writing
+  // buffer s % 2 at step s is safe: every wave finished reading it (step s - 2) before the
+  // barrier of step s - 1.
+  StepRegs r0, r1;
+  load_step(r0, 0);
+  if (kTK < a.k) load_step(r1, kTK);
+  for (int k0 = 0; k0 < a.k; k0 += 2 * kTK) {
+    consume(r0, 0, k0 + 2 * kTK);
+    if (k0 + kTK < a.k) consume(r1, 1, k0 + 3 * kTK);
   }
+
+  // epilogue: element i of a 32x32 tile sits at row (i/4)*8 + g*4 + i%4, column lc
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = rt * 32 + (i / 4) * 8 + g * 4 + (i % 4);
+      if (t.row0 + r >= t.n) continue;
+      const int64_t pos = t.p0 + t.row0 + r;
+      if constexpr (NMAT == 2) {
+        const float gv = acc[rt][0][i], uv = acc[rt][1][i];
+        const float hv = gv / (1.0f + __expf(-gv)) * uv;
+        static_cast<uint16_t*>(a.c)[pos * a.ldc + t.col0 + wave * 32 + lc] = (uint16_t)f32_to_bf16_rne(hv);
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          static_cast<float*>(a.c)[pos * a.ldc + t.col0 + wave * 64 + b * 32 + lc] = acc[rt][b][i];
+      }
+    }
 }
 
 // y[t] = sum_j w[t][j] * o[inv[t*K+j]] + g[t] * o[m*K + t]
@@ -298,8 +318,8 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(const float* o, const i
   *reinterpret_cast<f32x4*>(y + (int64_t)t * hidden + n4 * 4) = acc;
 }
 
-constexpr int kTNGate = 64;      // columns per matrix in the gate/up tiles
-constexpr int kTNDown = 128;     // columns in the down tiles
+constexpr int kTNGate = 128;     // columns per matrix in the gate/up tiles
+constexpr int kTNDown = 256;     // columns in the down tiles
 
 int grid_for(int m, int top_k, int n_exp, int shared, int nct) {
   // upper bound of row tiles: every group may waste one partial tile
@@ -330,7 +350,7 @@ hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s) {
   a.rows_per_expert = F; a.k = H;
   a.a = p.x; a.lda = H; a.a_by_token = 1;
   a.c = p.h; a.ldc = F;
-  hipLaunchKernelGGL((grouped_gemm_kernel<kTNGate, 2>), dim3(grid_for(p.m, K, L->n_experts, shared, F / kTNGate)),
+  hipLaunchKernelGGL((grouped_gemm_kernel<2>), dim3(grid_for(p.m, K, L->n_experts, shared, F / kTNGate)),
                      dim3(kPT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -342,7 +362,7 @@ hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s) {
   b.rows_per_expert = H; b.k = F;
   b.a = p.h; b.lda = F; b.a_by_token = 0;
   b.c = p.o; b.ldc = H;
-  hipLaunchKernelGGL((grouped_gemm_kernel<kTNDown, 1>), dim3(grid_for(p.m, K, L->n_experts, shared, H / kTNDown)),
+  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(grid_for(p.m, K, L->n_experts, shared, H / kTNDown)),
                      dim3(kPT), 0, s, b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 grid((H / 4 + 255) / 256, p.m);
