@@ -81,6 +81,11 @@ def quantize(fmt, w):
     return m
 
 
+def workspace(nbytes: int):
+    import torch
+    return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device="cuda")
+
+
 def timed(fn, steps, warmup):
     """Average ms per call of fn(i) over `steps` calls after `warmup` calls."""
     import torch
@@ -125,15 +130,18 @@ def run_mlp(args, m, mats, xb):
     h = torch.empty((m, INTER), dtype=torch.float32, device="cuda")
     y = torch.empty((m, HIDDEN), dtype=torch.bfloat16, device="cuda")
     R = len(mats)
+    g0, u0, d0 = mats[0]
+    ws_gu = workspace(bfq.bfp_gemm_workspace_bytes(g0, m, u0))
+    ws_d = workspace(bfq.bfp_gemm_workspace_bytes(d0, m))
 
     def step(i):
         g, u, d = mats[i % R]
-        bfq.bfp_gemm(g, x, w_up=u, out=h)
-        bfq.bfp_gemm(d, h, out_dtype=torch.bfloat16, out=y)
+        bfq.bfp_gemm(g, x, w_up=u, out=h, workspace=ws_gu)
+        bfq.bfp_gemm(d, h, out_dtype=torch.bfloat16, out=y, workspace=ws_d)
 
     def gateup(i):
         g, u, _ = mats[i % R]
-        bfq.bfp_gemm(g, x, w_up=u, out=h)
+        bfq.bfp_gemm(g, x, w_up=u, out=h, workspace=ws_gu)
 
     ms_step = timed(step, args.steps, args.warmup)
     ms_gu = timed(gateup, args.steps, args.warmup)
@@ -180,7 +188,8 @@ def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32"):
     for m, xb in xs_bits.items():
         x = bf16_dev(xb)
         y = torch.empty((m, base.n), dtype=torch.float32, device="cuda")
-        ms = timed(lambda i: bfq.bfp_gemm(mats[i % R], x, out=y), args.steps, args.warmup)
+        ws = workspace(bfq.bfp_gemm_workspace_bytes(base, m))
+        ms = timed(lambda i: bfq.bfp_gemm(mats[i % R], x, out=y, workspace=ws), args.steps, args.warmup)
         nbytes = base.nbytes + m * base.k * 2 + m * base.n * 4
         out[f"{name} M={m}"] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                 "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),

@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "BFP4", "BFP8", "BfpError", "BfpMatrix", "MoeLayer", "lib", "library_path",
-    "bfp_quantize", "bfp_dequantize", "bfp_gemm", "bfp_moe_route", "bfp_moe_dispatch",
+    "bfp_quantize", "bfp_dequantize", "bfp_gemm", "bfp_gemm_workspace_bytes", "bfp_moe_route", "bfp_moe_dispatch",
     "bfp_moe_workspace_bytes", "bfp_moe_forward", "exp_bytes", "code_bytes",
 ]
 
@@ -69,9 +69,12 @@ _SIGS = {
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "bfp_dequantize": (ctypes.c_int32, [ctypes.POINTER(_Tensor), ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    "bfp_gemm_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
+                                                  ctypes.c_int64]),
     "bfp_gemm": (ctypes.c_int32, [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
-                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
+                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p]),
     "bfp_moe_route_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_MoeLayer), ctypes.c_int64]),
     "bfp_moe_route": (ctypes.c_int32, [ctypes.POINTER(_MoeLayer), ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -185,9 +188,19 @@ def _dt(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def bfp_gemm_workspace_bytes(w: BfpMatrix, m: int, w_up: BfpMatrix | None = None) -> int:
+    vw = w.view()
+    vu = w_up.view() if w_up is not None else None
+    return int(lib().bfp_gemm_workspace_bytes(ctypes.byref(vw), ctypes.byref(vu) if vu is not None else None, m))
+
+
 def bfp_gemm(w: BfpMatrix, x: torch.Tensor, w_up: BfpMatrix | None = None, out_dtype=torch.float32,
-             out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """y = x W^T (or silu(x W^T) * (x Wup^T) when w_up is given); x is [m][k], m <= 32."""
+             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = x W^T (or silu(x W^T) * (x Wup^T) when w_up is given); x is [m][k], m <= 32.
+
+    ``workspace`` (uint8 device tensor of at least bfp_gemm_workspace_bytes bytes) is made
+    here when not given.
+    """
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a row-major [m][k] device tensor")
     m = x.shape[0]
@@ -195,9 +208,13 @@ def bfp_gemm(w: BfpMatrix, x: torch.Tensor, w_up: BfpMatrix | None = None, out_d
         out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
     vw = w.view()
     vu = w_up.view() if w_up is not None else None
+    if workspace is None:
+        need = bfp_gemm_workspace_bytes(w, m, w_up)
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
     st = lib().bfp_gemm(ctypes.byref(vw), ctypes.byref(vu) if vu is not None else None,
                         EPI_SWIGLU if w_up is not None else EPI_NONE,
-                        _ptr(x), _dt(x), m, x.stride(0), _ptr(out), _dt(out), out.stride(0), _stream(stream))
+                        _ptr(x), _dt(x), m, x.stride(0), _ptr(out), _dt(out), out.stride(0),
+                        _ptr(workspace), workspace.numel(), _stream(stream))
     _check("bfp_gemm", st)
     return out
 

@@ -104,9 +104,14 @@ int32_t bfp_dequantize(const bfp_tensor* w, int32_t out_dtype, void* out, void* 
                                       out, static_cast<hipStream_t>(stream)));
 }
 
+size_t bfp_gemm_workspace_bytes(const bfp_tensor* w, const bfp_tensor* w_up, int64_t m) {
+  if (check_tensor(w) != BFP_OK || m < 1 || m > BFP_GEMM_MAX_M) return 0;
+  return bfp::gemv_workspace_bytes(w->fmt, w_up != nullptr, w->n, w->k, m);
+}
+
 int32_t bfp_gemm(const bfp_tensor* w, const bfp_tensor* w_up, int32_t epilogue, const void* x,
                  int32_t x_dtype, int64_t m, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
-                 void* stream) {
+                 void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_tensor(w);
   if (st != BFP_OK) return st;
   if (epilogue == BFP_EPI_NONE) {
@@ -126,6 +131,9 @@ int32_t bfp_gemm(const bfp_tensor* w, const bfp_tensor* w_up, int32_t epilogue, 
   if (ldx < w->k || ldy < w->n) return BFP_E_SHAPE;
   const int64_t xs = x_dtype == BFP_DT_BF16 ? 2 : 4;
   if (!aligned16(x) || ((ldx * xs) % 16) != 0) return BFP_E_ALIGN;
+  const size_t need = bfp::gemv_workspace_bytes(w->fmt, epilogue == BFP_EPI_SWIGLU, w->n, w->k, m);
+  if (need > 0 && (!ws || ws_bytes < need)) return BFP_E_WORKSPACE;
+  if (ws && !aligned16(ws)) return BFP_E_ALIGN;
   bfp::GemvParams g;
   g.fmt = w->fmt;
   g.w_exp = w->exp; g.w_code = w->code;
@@ -134,6 +142,7 @@ int32_t bfp_gemm(const bfp_tensor* w, const bfp_tensor* w_up, int32_t epilogue, 
   g.n = w->n; g.k = w->k;
   g.x = x; g.ldx = ldx; g.x_bf16 = x_dtype == BFP_DT_BF16;
   g.m = m; g.y = y; g.ldy = ldy; g.y_bf16 = y_dtype == BFP_DT_BF16;
+  g.ws = ws;
   return from_hip(bfp::gemv_launch(g, static_cast<hipStream_t>(stream)));
 }
 

@@ -30,7 +30,11 @@ struct GemvParams {
   void* y;
   int64_t ldy;
   int y_bf16;
+  void* ws;                    // workspace of gemv_workspace_bytes bytes (or null when that is 0)
 };
+
+// Workspace bytes gemv_launch needs for these shapes (0: none).
+size_t gemv_workspace_bytes(int fmt, bool swiglu, int64_t n, int64_t k, int64_t m);
 
 hipError_t gemv_launch(const GemvParams& g, hipStream_t s);
 

@@ -1,6 +1,10 @@
-// Skinny BFP4/BFP8 matmul dispatch: picks the instantiation for the format and activation
-// type (the kernels themselves are in gemv_impl.hpp, compiled in four translation units).
+// Skinny BFP4/BFP8 matmul dispatch: the matrix-core kernel (mfma_gemv.hpp) or the vector-ALU
+// kernel (gemv_impl.hpp, compiled in four translation units).
+#include <stdlib.h>
+#include <string.h>
+
 #include "bfp_internal.hpp"
+#include "mfma_gemv.hpp"
 
 namespace bfp {
 
@@ -8,10 +12,60 @@ hipError_t gemv_launch_b4_bf16x(const GemvParams& g, hipStream_t s);
 hipError_t gemv_launch_b4_f32x(const GemvParams& g, hipStream_t s);
 hipError_t gemv_launch_b8_bf16x(const GemvParams& g, hipStream_t s);
 hipError_t gemv_launch_b8_f32x(const GemvParams& g, hipStream_t s);
+hipError_t mfma_gemv_launch_b4(const mg::MgArgs& a, bool x_bf16, hipStream_t s);
+hipError_t mfma_gemv_launch_b8(const mg::MgArgs& a, bool x_bf16, hipStream_t s);
 
-hipError_t gemv_launch(const GemvParams& g, hipStream_t s) {
+namespace {
+
+// One activation row runs the vector-ALU kernel (it streams the weights faster when there is
+// a single row to multiply); 2..32 rows run the matrix-core kernel. BFP_GEMV_KERNEL=vector or
+// =mfma forces one kernel for every m (for measurement).
+enum class Kernel { kAuto, kVector, kMfma };
+Kernel forced() {
+  static const Kernel k = [] {
+    const char* e = getenv("BFP_GEMV_KERNEL");
+    if (e && strcmp(e, "vector") == 0) return Kernel::kVector;
+    if (e && strcmp(e, "mfma") == 0) return Kernel::kMfma;
+    return Kernel::kAuto;
+  }();
+  return k;
+}
+bool use_vector(int64_t m) {
+  const Kernel k = forced();
+  return k == Kernel::kVector || (k == Kernel::kAuto && m == 1);
+}
+
+hipError_t vector_launch(const GemvParams& g, hipStream_t s) {
   if (g.fmt == 4) return g.x_bf16 ? gemv_launch_b4_bf16x(g, s) : gemv_launch_b4_f32x(g, s);
   return g.x_bf16 ? gemv_launch_b8_bf16x(g, s) : gemv_launch_b8_f32x(g, s);
+}
+
+hipError_t mfma_launch(const GemvParams& g, hipStream_t s) {
+  mg::MgArgs a;
+  a.exp[0] = g.w_exp; a.code[0] = g.w_code;
+  a.exp[1] = g.u_exp; a.code[1] = g.u_code;
+  a.x = g.x; a.ldx = g.ldx;
+  a.y = g.y; a.ldy = g.ldy;
+  a.n = (int)g.n; a.k = (int)g.k; a.m = (int)g.m;
+  a.y_bf16 = g.y_bf16;
+  a.ws = static_cast<float*>(g.ws);
+  a.ks = 1; a.sps = 0; a.kc = 0; a.exp_vec = 0;
+  a.code16 = (g.k % 32) == 0;
+  return g.fmt == 4 ? mfma_gemv_launch_b4(a, g.x_bf16 != 0, s) : mfma_gemv_launch_b8(a, g.x_bf16 != 0, s);
+}
+
+}  // namespace
+
+size_t gemv_workspace_bytes(int fmt, bool swiglu, int64_t n, int64_t k, int64_t m) {
+  if (use_vector(m)) return 0;
+  const int N = (int)n, K = (int)k, M = (int)m;
+  if (fmt == 4) return swiglu ? mg::workspace_bytes<4, 2>(N, K, M) : mg::workspace_bytes<4, 1>(N, K, M);
+  return swiglu ? mg::workspace_bytes<8, 2>(N, K, M) : mg::workspace_bytes<8, 1>(N, K, M);
+}
+
+hipError_t gemv_launch(const GemvParams& g, hipStream_t s) {
+  if (use_vector(g.m)) return vector_launch(g, s);
+  return mfma_launch(g, s);
 }
 
 }  // namespace bfp

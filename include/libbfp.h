@@ -56,7 +56,7 @@ typedef enum {
   BFP_E_SHAPE = 2,        /* k not a multiple of 16, m or n out of range, mismatched shapes */
   BFP_E_ALIGN = 3,        /* a device pointer is not 16-byte aligned */
   BFP_E_NONFINITE = 4,    /* bfp_quantize met Inf or NaN (outputs are then unspecified) */
-  BFP_E_WORKSPACE = 5,    /* workspace missing or smaller than bfp_moe_workspace_bytes */
+  BFP_E_WORKSPACE = 5,    /* workspace missing or smaller than the *_workspace_bytes query */
   BFP_E_DEVICE = 6,       /* a HIP runtime call or kernel launch failed */
   BFP_E_UNSUPPORTED = 7   /* a valid request this build does not implement */
 } bfp_status;
@@ -108,17 +108,31 @@ int32_t bfp_quantize(int32_t fmt, const float *w, int64_t n, int64_t k,
 int32_t bfp_dequantize(const bfp_tensor *w, int32_t out_dtype, void *out, void *stream);
 
 /*
+ * Workspace bytes bfp_gemm needs for an m-row call on w (with w_up for SWIGLU, else NULL);
+ * 0 when it needs none. Depends on the shapes only (not on pointers or values).
+ */
+size_t bfp_gemm_workspace_bytes(const bfp_tensor *w, const bfp_tensor *w_up, int64_t m);
+
+/*
  * Skinny matmul over streamed BFP weights, dequantized in registers:
  *   epilogue NONE  : y[i][j] = sum_k x[i][k] * W[j][k]
  *   epilogue SWIGLU: y[i][j] = silu(sum_k x[i][k] * W[j][k]) * (sum_k x[i][k] * Wup[j][k])
  * with silu(g) = g / (1 + e^-g). i < m (1..BFP_GEMM_MAX_M rows share one pass over the
  * weights), j < w->n, k < w->k. x: device [m][ldx] of x_dtype (bf16 or fp32); y: device
- * [m][ldy] of y_dtype (fp32, or bf16 rounded to nearest even). Products are exact and
- * sums are fp32. w_up must be NULL for NONE and match w's format and shape for SWIGLU.
+ * [m][ldy] of y_dtype (fp32, or bf16 rounded to nearest even). Products of bf16 x with the
+ * weights are exact and sums are fp32. m = 1 runs on the vector ALUs (fp32 x exact as well);
+ * m >= 2 runs on the bf16 matrix cores, where fp32 x enters as the sum of two bf16 values
+ * (about 16 significant bits) and row i of the result does not depend on m or on the other
+ * rows (same reduction order for every m in 2..32). w_up must be NULL for NONE and match w's
+ * format and shape for
+ * SWIGLU. ws: device workspace of at least bfp_gemm_workspace_bytes(w, w_up, m) bytes (may
+ * be NULL when that is 0; BFP_E_WORKSPACE if missing or smaller), 16-byte aligned, contents
+ * on entry and on return unspecified. Calls sharing a workspace on different streams race.
  */
 int32_t bfp_gemm(const bfp_tensor *w, const bfp_tensor *w_up, int32_t epilogue,
                  const void *x, int32_t x_dtype, int64_t m, int64_t ldx,
-                 void *y, int32_t y_dtype, int64_t ldy, void *stream);
+                 void *y, int32_t y_dtype, int64_t ldy, void *ws, size_t ws_bytes,
+                 void *stream);
 
 /*
  * One MoE layer with BFP4 experts ("qwen3.6-a3b-blackhole", introduction; "Qwen3.6-35B-A3B

@@ -61,17 +61,24 @@ def test_host_validation_before_any_launch():
     assert lib.bfp_dequantize(ctypes.byref(t), 7, 16, None) == 1
     # gemm
     w = _tensor()
-    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 0, 64, 16, 0, 32, None) == 2     # m = 0
-    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 33, 64, 16, 0, 32, None) == 2    # m > 32
-    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 1, 32, 16, 0, 32, None) == 2     # ldx < k
-    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 1, 68, 16, 0, 32, None) == 3     # ldx*2 % 16
-    assert lib.bfp_gemm(ctypes.byref(w), None, 1, 16, 1, 1, 64, 16, 0, 32, None) != 0     # SwiGLU without up
+    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 0, 64, 16, 0, 32, None, 0, None) == 2     # m = 0
+    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 33, 64, 16, 0, 32, None, 0, None) == 2    # m > 32
+    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 1, 32, 16, 0, 32, None, 0, None) == 2     # ldx < k
+    assert lib.bfp_gemm(ctypes.byref(w), None, 0, 16, 1, 1, 68, 16, 0, 32, None, 0, None) == 3     # ldx*2 % 16
+    assert lib.bfp_gemm(ctypes.byref(w), None, 1, 16, 1, 1, 64, 16, 0, 32, None, 0, None) != 0     # SwiGLU without up
     u = _tensor(n=16)
-    assert lib.bfp_gemm(ctypes.byref(w), ctypes.byref(u), 1, 16, 1, 1, 64, 16, 0, 32, None) == 2
+    assert lib.bfp_gemm(ctypes.byref(w), ctypes.byref(u), 1, 16, 1, 1, 64, 16, 0, 32, None, 0, None) == 2
     u = _tensor(fmt=8)
-    assert lib.bfp_gemm(ctypes.byref(w), ctypes.byref(u), 1, 16, 1, 1, 64, 16, 0, 32, None) == 1
-    assert lib.bfp_gemm(ctypes.byref(w), ctypes.byref(w), 0, 16, 1, 1, 64, 16, 0, 32, None) == 1
-    assert lib.bfp_gemm(ctypes.byref(w), None, 3, 16, 1, 1, 64, 16, 0, 32, None) == 1
+    assert lib.bfp_gemm(ctypes.byref(w), ctypes.byref(u), 1, 16, 1, 1, 64, 16, 0, 32, None, 0, None) == 1
+    assert lib.bfp_gemm(ctypes.byref(w), ctypes.byref(w), 0, 16, 1, 1, 64, 16, 0, 32, None, 0, None) == 1
+    assert lib.bfp_gemm(ctypes.byref(w), None, 3, 16, 1, 1, 64, 16, 0, 32, None, 0, None) == 1
+    # a shape that is cut into K slices needs the workspace it reports
+    big = _tensor(n=64, k=16384)
+    need = lib.bfp_gemm_workspace_bytes(ctypes.byref(big), None, 2)
+    assert need > 0
+    assert lib.bfp_gemm(ctypes.byref(big), None, 0, 16, 1, 2, 16384, 16, 0, 64, None, 0, None) == 5
+    assert lib.bfp_gemm(ctypes.byref(big), None, 0, 16, 1, 2, 16384, 16, 0, 64, 16, need - 1, None) == 5
+    assert lib.bfp_gemm_workspace_bytes(ctypes.byref(big), None, 0) == 0             # m out of range
 
 
 def test_python_binding_refuses_without_library(monkeypatch, tmp_path):

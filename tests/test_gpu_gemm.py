@@ -93,12 +93,53 @@ def test_gemm_one_hot_bit_exact(fmt):
 
 
 def test_gemm_rows_are_independent_of_m():
-    """Row i of an m-row call equals the same row computed alone (same reduction order)."""
+    """Row i of an m-row call (2 <= m <= 32, the matrix-core kernel) does not depend on m or on
+    the other rows: same reduction order for every m. A one-row call runs the vector kernel
+    and agrees within the tolerance."""
     note("gemm batch invariance")
     wm, wd, x64, xt = _case(BFP4, 150, 4096, 8, seed=77)
     y8 = bfq.bfp_gemm(wm, xt).cpu().numpy()
-    y1 = np.stack([bfq.bfp_gemm(wm, xt[i:i + 1].contiguous()).cpu().numpy()[0] for i in range(8)])
-    assert np.array_equal(y8.view(np.uint32), y1.view(np.uint32))
+    for i in range(0, 8, 2):
+        y2 = bfq.bfp_gemm(wm, xt[i:i + 2].contiguous()).cpu().numpy()
+        assert np.array_equal(y8[i:i + 2].view(np.uint32), y2.view(np.uint32))
+    y1 = bfq.bfp_gemm(wm, xt[3:4].contiguous()).cpu().numpy()
+    assert_within(y1, oracle.gemm(x64[3:4], wd), oracle.normaliser(x64[3:4], wd), TOL, what="gemm m=1")
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_gemm_rows_independent_of_m_long_k(x_dtype):
+    """Same property on a long-K shape whose K is cut into slices, for m up to 32 (two row
+    tiles) and for fp32 activations (hi + lo planes)."""
+    note(f"gemm batch invariance long K {x_dtype}")
+    wm, wd, x64, xt = _case(BFP4, 96, 17408, 32, seed=91, x_dtype=x_dtype)
+    y32 = bfq.bfp_gemm(wm, xt).cpu().numpy()
+    y7 = bfq.bfp_gemm(wm, xt[5:12].contiguous()).cpu().numpy()
+    y2 = bfq.bfp_gemm(wm, xt[20:22].contiguous()).cpu().numpy()
+    assert np.array_equal(y32[5:12].view(np.uint32), y7.view(np.uint32))
+    assert np.array_equal(y32[20:22].view(np.uint32), y2.view(np.uint32))
+    assert_within(y32, oracle.gemm(x64, wd), oracle.normaliser(x64, wd), TOL, what="gemm long K")
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+@pytest.mark.parametrize("wscale,xscale", [(2.0 ** -128, 2.0 ** 60), (2.0 ** -124, 2.0 ** 50),
+                                           (2.0 ** 121, 2.0 ** -100)])
+def test_gemm_extreme_exponents(fmt, wscale, xscale):
+    """Shared exponents far from 1 (fp32 subnormal weights, E < 8, E > 247) mixed with all-zero
+    blocks: the unpack must stay exact outside the range of the fast conversion. x is scaled so
+    that the products stay normal fp32 numbers."""
+    note(f"gemm extreme exponents fmt={fmt} w={wscale:.3g} x={xscale:.3g}")
+    n, k, m = 80, 1024, 3
+    rng = np.random.default_rng(17 + fmt)
+    w = rng.standard_normal((n, k)) * wscale
+    w[np.repeat(rng.random((n, k // 16)) < 0.25, 16, axis=1)] = 0.0
+    w = w.astype(np.float32)
+    exp, code = oracle.encode(w, fmt)
+    wd = oracle.decode(exp, code, fmt, n, k)
+    assert np.count_nonzero(wd) > n * k // 2
+    xb = synth.bf16_bits((rng.standard_normal((m, k)) * xscale).astype(np.float32))
+    x64 = oracle.bf16_to_f64(xb)
+    y = bfq.bfp_gemm(matrix_from_oracle(fmt, exp, code, n, k), dev_bf16(xb)).cpu().numpy()
+    assert_within(y, oracle.gemm(x64, wd), oracle.normaliser(x64, wd), TOL, what="gemm extreme exponents")
 
 
 def test_gemm_deterministic():
