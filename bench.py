@@ -51,7 +51,100 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows per matrix in the CPU sample")
+    ap.add_argument("--pmc-driver", action="store_true",
+                    help="only launch the headline gate/up kernel and a 512 MiB copy (run under rocprofv3 --pmc)")
+    ap.add_argument("--pmc-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of --pmc-driver "
+                         "into the traffic summary")
     return ap.parse_args()
+
+
+# ---- HBM traffic of the headline kernel (rocprofv3 counters) ------------------------------
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_bfp4_gateup_m1_hbm_traffic.md")
+HEADLINE_SOURCES = ("block_float_quantized_amd/csrc/gemv_impl.hpp", "block_float_quantized_amd/csrc/gemv_b4_bf16x.hip",
+                    "block_float_quantized_amd/csrc/bfp_device.hpp", "block_float_quantized_amd/csrc/gemv.hip")
+HEADLINE_KERNEL = "gemv_kernel<4, 1, 1, 16, 2, 2, 2, true, 256>"
+COPY_BYTES = 512 << 20
+
+
+def headline_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in HEADLINE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter summary, or None
+    when there is none or the kernel's sources changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines() if l.startswith(("traffic_bytes_per_launch:",
+                                                                              "kernel_sources_sha256:")))
+    if fields.get("kernel_sources_sha256", "").strip() != headline_sources_sha256():
+        return None
+    return int(fields["traffic_bytes_per_launch"].strip())
+
+
+def pmc_driver():
+    """Launch the headline gate/up kernel over cold replicas and a plain copy of known size."""
+    import torch
+    import block_float_quantized_amd as bfq
+    torch.cuda.set_device(0)
+    c, mats = make_mlp(8)
+    x = bf16_dev(c["x"])
+    h = torch.empty((1, INTER), dtype=torch.float32, device="cuda")
+    for i in range(24):
+        g, u, _ = mats[i % len(mats)]
+        bfq.bfp_gemm(g, x, w_up=u, out=h)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log("pmc driver done")
+
+
+def pmc_report(fetch_dir: str, write_dir: str):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the headline kernel and of the copy;
+    the copy (COPY_BYTES read and written) calibrates each counter to bytes."""
+    import glob
+    import sqlite3
+
+    def averages(d, counter):
+        db = glob.glob(os.path.join(d, "**", "*.db"), recursive=True)[0]
+        rows = sqlite3.connect(db).execute(
+            "select kernel_name, counter_name, value from counters_collection").fetchall()
+        acc = {}
+        for name, cn, v in rows:
+            if cn != counter:
+                continue
+            key = "headline" if HEADLINE_KERNEL in name else "copy" if "MulFunctor" in name else None
+            if key:
+                acc.setdefault(key, []).append(v)
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    f, fn = averages(fetch_dir, "FETCH_SIZE")
+    w, wn = averages(write_dir, "WRITE_SIZE")
+    kib = COPY_BYTES / 1024
+    ff, fw = kib / f["copy"], kib / w["copy"]
+    fetch_b = f["headline"] * 1024 * ff
+    write_b = w["headline"] * 1024 * fw
+    import block_float_quantized_amd as bfq
+    alg = 2 * (bfq.exp_bytes(INTER, HIDDEN) + bfq.code_bytes(4, INTER, HIDDEN)) + HIDDEN * 2 + INTER * 4
+    print(f"headline kernel: {HEADLINE_KERNEL} ({fn['headline']} dispatches), copy: {fn['copy']} dispatches")
+    print(f"FETCH_SIZE KiB/dispatch: headline {f['headline']:.1f}, copy {f['copy']:.1f} "
+          f"(copy reads {kib:.0f} KiB: factor {ff:.4f})")
+    print(f"WRITE_SIZE KiB/dispatch: headline {w['headline']:.1f}, copy {w['copy']:.1f} "
+          f"(copy writes {kib:.0f} KiB: factor {fw:.4f})")
+    print(f"scaled HBM bytes per launch: read {fetch_b:.0f}, written {write_b:.0f}; algorithmic {alg}")
+    print(f"traffic_bytes_per_launch: {int(round(fetch_b + write_b))}")
+    print(f"kernel_sources_sha256: {headline_sources_sha256()}")
 
 
 def log(msg):
@@ -265,9 +358,15 @@ def moe_workloads(args):
 
 def main():
     args = parse()
+    if args.pmc_report:
+        pmc_report(*args.pmc_report)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}), flush=True)
         sys.exit(2)
+    if args.pmc_driver:
+        pmc_driver()
+        return
     import torch
     import block_float_quantized_amd as bfq
     import synth
@@ -321,7 +420,8 @@ def main():
                                f"BFP4 + SwiGLU (fp32 h), down 17408x5120 BFP4, bf16 out",
                    "M": args.M, "replicas": 8, "bytes_per_step": head["bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(head["gateup_GB/s"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(head["gateup_GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(head["gateup_GB/s"] / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic() if args.M == 1 else None,
                      "kernel": "gemv_kernel BFP4 gate+up+SwiGLU", "avg_us": round(head["gateup_us"], 2)},
         "workloads": workloads,
     }
