@@ -60,35 +60,37 @@ struct PfArgs {
 };
 
 // 16 BFP4 values (two dwords) with exponent E -> 8 dwords of bf16 pairs in the permuted order
-// (v0,v2)(v4,v6)(v1,v3)(v5,v7) per 8 values.
-__device__ __forceinline__ void dequant16(uint32_t c0, uint32_t c1, uint32_t e, uint32_t* out) {
-  if (e >= 8 && e <= 247) {
-    const float sc = __uint_as_float((e + 7u) << 23);           // 2^(E - 120)
-    const uint32_t cc[2] = {c0, c1};
+// (v0,v2)(v4,v6)(v1,v3)(v5,v7) per 8 values. Fast form, for E in [8, 247]: the scaled FP8
+// conversion applies 2^(E-120) (a normal fp32) and every result is a normal bf16.
+__device__ __forceinline__ void dequant16_fast(uint32_t c0, uint32_t c1, uint32_t e, uint32_t* out) {
+  const float sc = __uint_as_float((e + 7u) << 23);           // 2^(E - 120)
+  const uint32_t cc[2] = {c0, c1};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t c = cc[h];
-      const uint32_t ev = ((c << 4) & 0x80808080u) | (c & 0x07070707u);
-      const uint32_t od = (c & 0x80808080u) | ((c >> 4) & 0x07070707u);
-      out[4 * h + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, false));
-      out[4 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, true));
-      out[4 * h + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, false));
-      out[4 * h + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, true));
-    }
-  } else {
-    const int sh = (int)e - 120;
-    float v[16];
-    unpack8_bfp4(c0, v);
-    unpack8_bfp4(c1, v + 8);
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t c = cc[h];
+    const uint32_t ev = ((c << 4) & 0x80808080u) | (c & 0x07070707u);
+    const uint32_t od = (c & 0x80808080u) | ((c >> 4) & 0x07070707u);
+    out[4 * h + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, false));
+    out[4 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, true));
+    out[4 * h + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, false));
+    out[4 * h + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, true));
+  }
+}
+
+// Any exponent: fp32 values scaled by ldexp (exact, subnormals included), top halves packed.
+__device__ __forceinline__ void dequant16_any(uint32_t c0, uint32_t c1, uint32_t e, uint32_t* out) {
+  const int sh = (int)e - 120;
+  float v[16];
+  unpack8_bfp4(c0, v);
+  unpack8_bfp4(c1, v + 8);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float* w = v + 8 * h;
-      auto b = [&](int i) { return __float_as_uint(__builtin_amdgcn_ldexpf(w[i], sh)) >> 16; };
-      out[4 * h + 0] = b(0) | (b(2) << 16);
-      out[4 * h + 1] = b(4) | (b(6) << 16);
-      out[4 * h + 2] = b(1) | (b(3) << 16);
-      out[4 * h + 3] = b(5) | (b(7) << 16);
-    }
+  for (int h = 0; h < 2; ++h) {
+    const float* w = v + 8 * h;
+    auto b = [&](int i) { return __float_as_uint(__builtin_amdgcn_ldexpf(w[i], sh)) >> 16; };
+    out[4 * h + 0] = b(0) | (b(2) << 16);
+    out[4 * h + 1] = b(4) | (b(6) << 16);
+    out[4 * h + 2] = b(1) | (b(3) << 16);
+    out[4 * h + 3] = b(5) | (b(7) << 16);
   }
 }
 
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(kPT) void grouped_gemm_kernel(PfArgs a) {
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      R.rc[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bcode[b] + (k0 + 32 * g) / 2));
+      R.rc[b] = *reinterpret_cast<const u32x4*>(bcode[b] + (k0 + 32 * g) / 2);
       R.re[b] = *reinterpret_cast<const uint16_t*>(bexp[b] + (k0 + 32 * g) / 16);
     }
   };
@@ -235,10 +237,22 @@ __global__ __launch_bounds__(kPT) void grouped_gemm_kernel(PfArgs a) {
   // step two ahead is issued before the MFMAs
   auto consume = [&](StepRegs& R, int buf, int k_next2) {
     uint32_t dq[NB][16];
+    // one decision per wave and step: all exponents inside the fast conversion's range?
+    bool ok = true;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      dequant16(R.rc[b].x, R.rc[b].y, R.re[b] & 0xffu, dq[b]);
-      dequant16(R.rc[b].z, R.rc[b].w, R.re[b] >> 8, dq[b] + 8);
+    for (int b = 0; b < NB; ++b) ok = ok && ((R.re[b] & 0xffu) - 8u) <= 239u && ((R.re[b] >> 8) - 8u) <= 239u;
+    if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        dequant16_fast(R.rc[b].x, R.rc[b].y, R.re[b] & 0xffu, dq[b]);
+        dequant16_fast(R.rc[b].z, R.rc[b].w, R.re[b] >> 8, dq[b] + 8);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        dequant16_any(R.rc[b].x, R.rc[b].y, R.re[b] & 0xffu, dq[b]);
+        dequant16_any(R.rc[b].z, R.rc[b].w, R.re[b] >> 8, dq[b] + 8);
+      }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(&As[buf][ar][aq * 16 + h * 8]) = permute8(R.ra[h]);
@@ -264,12 +278,13 @@ __global__ __launch_bounds__(kPT) void grouped_gemm_kernel(PfArgs a) {
   // two register sets, two LDS buffers: step s uses set s % 2 and buffer s % 2. Writing
   // buffer s % 2 at step s is safe: every wave finished reading it (step s - 2) before the
   // barrier of step s - 1.
+  // (K is a multiple of 2 kTK: the loop body is the same for every iteration)
   StepRegs r0, r1;
   load_step(r0, 0);
-  if (kTK < a.k) load_step(r1, kTK);
+  load_step(r1, kTK);
   for (int k0 = 0; k0 < a.k; k0 += 2 * kTK) {
     consume(r0, 0, k0 + 2 * kTK);
-    if (k0 + kTK < a.k) consume(r1, 1, k0 + 3 * kTK);
+    consume(r1, 1, k0 + 3 * kTK);
   }
 
   // epilogue: element i of a 32x32 tile sits at row (i/4)*8 + g*4 + i%4, column lc

@@ -170,6 +170,7 @@ size_t bfp_moe_route_workspace_bytes(const bfp_moe_layer *L, int64_t m);
  * x: device bf16 [m][hidden]; ids: device int32 [m][top_k]; w: device fp32 [m][top_k];
  * g: device fp32 [m] or NULL; ws: device workspace of at least
  * bfp_moe_route_workspace_bytes(L, m) bytes. Only the router fields of L are read.
+ * m > BFP_GEMM_MAX_M needs hidden % 64 == 0 (else BFP_E_UNSUPPORTED).
  */
 int32_t bfp_moe_route(const bfp_moe_layer *L, const uint16_t *x, int64_t m,
                       int32_t *ids, float *w, float *g, void *ws, size_t ws_bytes, void *stream);
@@ -196,7 +197,8 @@ size_t bfp_moe_workspace_bytes(const bfp_moe_layer *L, int64_t m);
  * for all tokens that chose it. m <= 32 runs the skinny decode path (h = silu(gate)*up kept
  * in fp32); larger m runs the prefill path, where tokens are grouped by expert and h is
  * rounded to bf16 (nearest even) before the down projection, which is then a bf16
- * matrix-core product with fp32 accumulation.
+ * matrix-core product with fp32 accumulation; it needs hidden % 256 == 0 and inter % 128 == 0
+ * (else BFP_E_UNSUPPORTED).
  * x: device bf16 [m][hidden]; y: device fp32 [m][hidden]; topk_ids / topk_w: optional
  * device outputs [m][top_k] (NULL to skip); ws: device workspace of at least
  * bfp_moe_workspace_bytes(L, m) bytes (contents on return unspecified).
