@@ -29,13 +29,16 @@
 #include "bfp_moe.hpp"
 #include "bfp_prefill.hpp"
 
+#include <type_traits>
+
 namespace bfp {
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kTM = 64;          // rows (pairs) per tile
+constexpr int kTM = 128;         // rows (pairs) per tile
+constexpr int kRT = kTM / 32;    // 32-row MFMA fragments per tile
 constexpr int kTK = 64;          // K per step
 constexpr int kLDK = kTK + 8;    // bf16 per LDS row (padding spreads banks)
 constexpr int kPT = 256;         // threads per workgroup
@@ -59,39 +62,28 @@ struct PfArgs {
   int64_t ldc;
 };
 
-// 16 BFP4 values (two dwords) with exponent E -> 8 dwords of bf16 pairs in the permuted order
-// (v0,v2)(v4,v6)(v1,v3)(v5,v7) per 8 values. Fast form, for E in [8, 247]: the scaled FP8
-// conversion applies 2^(E-120) (a normal fp32) and every result is a normal bf16.
-__device__ __forceinline__ void dequant16_fast(uint32_t c0, uint32_t c1, uint32_t e, uint32_t* out) {
+// 8 BFP4 values (one dword) with exponent E -> 4 dwords of bf16 pairs in the permuted order
+// (v0,v2)(v4,v6)(v1,v3)(v5,v7). Fast form, for E in [8, 247]: the scaled FP8 conversion
+// applies 2^(E-120) (a normal fp32) and every result is a normal bf16.
+__device__ __forceinline__ u32x4 dequant8_fast(uint32_t c, uint32_t e) {
   const float sc = __uint_as_float((e + 7u) << 23);           // 2^(E - 120)
-  const uint32_t cc[2] = {c0, c1};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t c = cc[h];
-    const uint32_t ev = ((c << 4) & 0x80808080u) | (c & 0x07070707u);
-    const uint32_t od = (c & 0x80808080u) | ((c >> 4) & 0x07070707u);
-    out[4 * h + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, false));
-    out[4 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, true));
-    out[4 * h + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, false));
-    out[4 * h + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, true));
-  }
+  const uint32_t ev = ((c << 4) & 0x80808080u) | (c & 0x07070707u);
+  const uint32_t od = (c & 0x80808080u) | ((c >> 4) & 0x07070707u);
+  u32x4 o;
+  o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, false));
+  o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, true));
+  o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, false));
+  o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, true));
+  return o;
 }
 
 // Any exponent: fp32 values scaled by ldexp (exact, subnormals included), top halves packed.
-__device__ __forceinline__ void dequant16_any(uint32_t c0, uint32_t c1, uint32_t e, uint32_t* out) {
+__device__ __forceinline__ u32x4 dequant8_any(uint32_t c, uint32_t e) {
   const int sh = (int)e - 120;
-  float v[16];
-  unpack8_bfp4(c0, v);
-  unpack8_bfp4(c1, v + 8);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float* w = v + 8 * h;
-    auto b = [&](int i) { return __float_as_uint(__builtin_amdgcn_ldexpf(w[i], sh)) >> 16; };
-    out[4 * h + 0] = b(0) | (b(2) << 16);
-    out[4 * h + 1] = b(4) | (b(6) << 16);
-    out[4 * h + 2] = b(1) | (b(3) << 16);
-    out[4 * h + 3] = b(5) | (b(7) << 16);
-  }
+  float w[8];
+  unpack8_bfp4(c, w);
+  auto b = [&](int i) { return __float_as_uint(__builtin_amdgcn_ldexpf(w[i], sh)) >> 16; };
+  return u32x4{b(0) | (b(2) << 16), b(4) | (b(6) << 16), b(1) | (b(3) << 16), b(5) | (b(7) << 16)};
 }
 
 // 8 bf16 activations (natural order) -> the same permutation as the weights.
@@ -153,7 +145,7 @@ __device__ __forceinline__ bool find_tile(const PfArgs& a, TileInfo& t) {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Grouped GEMM C[pos][col] = A[row(pos)] . W_e[col] for one tile of kTM rows, on
-// v_mfma_f32_32x32x16_bf16. Each of the 4 waves owns all kTM rows (two 32-row A fragments)
+// v_mfma_f32_32x32x16_bf16. Each of the 4 waves owns all kTM rows (kRT 32-row A fragments)
 // and NB = 2 B tiles of 32 columns: NMAT = 2 -> the same 32 columns of gate and of up (the
 // SwiGLU pair lands in one lane), NMAT = 1 -> 64 adjacent columns. A workgroup therefore
 // covers TN = 4 * 32 * 2 / NMAT columns of each matrix.
@@ -163,7 +155,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // in registers, so the weights never touch LDS. Lane group g = lane / 32 takes K values
 // [32g, 32g + 32) of the step, 8 per MFMA; its A fragment reads the same K values from LDS.
 template <int NMAT>
-__global__ __launch_bounds__(kPT) void grouped_gemm_kernel(PfArgs a) {
+__global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
   constexpr int NB = 2;                            // 32-column B tiles per wave
   constexpr int TN = 4 * 32 * NB / NMAT;           // columns per matrix per workgroup
   __shared__ __align__(16) uint16_t As[2][kTM][kLDK];
@@ -202,72 +194,76 @@ __global__ __launch_bounds__(kPT) void grouped_gemm_kernel(PfArgs a) {
     bcode[b] = codeb[mat] + (int64_t)col * (a.k / 2);
     bexp[b] = expb[mat] + (int64_t)col * nbk;
   }
-  // A staging: 64 rows x 64 values = 256 threads x 16 values
-  const int ar = tid / 4, aq = tid % 4;
+  // A staging: kTM rows x 64 values = 256 threads x 32 values
+  constexpr int kAQ = kPT / kTM;                   // threads per row
+  constexpr int kAH = 64 / kAQ / 8;                // 8-value pieces per thread
+  const int ar = tid / kAQ, aq = tid % kAQ;
   const int arow_this = arow[ar];
+  // rows of this tile that exist (wave-uniform): MFMAs of fragments past them are skipped
+  const int nrt = (min(kTM, t.n - t.row0) + 31) / 32;
 
-  // global loads of one K step, kept in registers until the step is consumed
+  // weight loads of one K step (issued two steps ahead), kept in registers until consumed;
+  // activation loads of the next step (one step ahead) go to one register set
   struct StepRegs {
-    uint4 ra[2];
     u32x4 rc[NB];
     uint32_t re[NB];
   };
   auto load_step = [&](StepRegs& R, int k0) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      R.ra[h] = make_uint4(0, 0, 0, 0);
-      if (arow_this >= 0)
-        R.ra[h] = *reinterpret_cast<const uint4*>(a.a + (int64_t)arow_this * a.lda + k0 + aq * 16 + h * 8);
-    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       R.rc[b] = *reinterpret_cast<const u32x4*>(bcode[b] + (k0 + 32 * g) / 2);
       R.re[b] = *reinterpret_cast<const uint16_t*>(bexp[b] + (k0 + 32 * g) / 16);
     }
   };
-
-  f32x16 acc[2][NB];
+  uint4 ra[kAH];
+  auto load_a = [&](int k0) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int h = 0; h < kAH; ++h) {
+      ra[h] = make_uint4(0, 0, 0, 0);
+      if (arow_this >= 0)
+        ra[h] = *reinterpret_cast<const uint4*>(a.a + (int64_t)arow_this * a.lda + k0 + aq * 8 * kAH + h * 8);
+    }
+  };
+
+  f32x16 acc[kRT][NB];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[rt][b] = f32x16{};
 
-  // consume one step: dequantize B, stage A into LDS buffer `buf`, one barrier, MFMAs; the
-  // registers of the step are free again once the barrier is passed, so the load of the
-  // step two ahead is issued before the MFMAs
-  auto consume = [&](StepRegs& R, int buf, int k_next2) {
-    uint32_t dq[NB][16];
+  // consume step k0: stage its activations into LDS buffer `buf`, one barrier, then issue the
+  // loads of the next step's activations and of the weights two steps ahead, then dequantize
+  // and run the MFMAs of the NRT fragments that hold rows
+  auto consume = [&](StepRegs& R, int buf, int k0, auto NC) __attribute__((always_inline)) {
+    constexpr int NRT = decltype(NC)::value;
     // one decision per wave and step: all exponents inside the fast conversion's range?
     bool ok = true;
 #pragma unroll
     for (int b = 0; b < NB; ++b) ok = ok && ((R.re[b] & 0xffu) - 8u) <= 239u && ((R.re[b] >> 8) - 8u) <= 239u;
-    if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
+    const bool fast = __builtin_amdgcn_ballot_w64(!ok) == 0;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        dequant16_fast(R.rc[b].x, R.rc[b].y, R.re[b] & 0xffu, dq[b]);
-        dequant16_fast(R.rc[b].z, R.rc[b].w, R.re[b] >> 8, dq[b] + 8);
-      }
-    } else {
+    for (int h = 0; h < kAH; ++h) *reinterpret_cast<uint4*>(&As[buf][ar][aq * 8 * kAH + h * 8]) = permute8(ra[h]);
+    u32x4 cw[NB];
+    uint32_t ew[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        dequant16_any(R.rc[b].x, R.rc[b].y, R.re[b] & 0xffu, dq[b]);
-        dequant16_any(R.rc[b].z, R.rc[b].w, R.re[b] >> 8, dq[b] + 8);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(&As[buf][ar][aq * 16 + h * 8]) = permute8(R.ra[h]);
+    for (int b = 0; b < NB; ++b) { cw[b] = R.rc[b]; ew[b] = R.re[b]; }
     __syncthreads();
-    if (k_next2 < a.k) load_step(R, k_next2);
+    if (k0 + kTK < a.k) load_a(k0 + kTK);
+    if (k0 + 2 * kTK < a.k) load_step(R, k0 + 2 * kTK);
+    // per 16-value MFMA slice: dequantize 8 values of each B tile, then the MFMAs
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       bf16x8 bf[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const u32x4 v = u32x4{dq[b][4 * st], dq[b][4 * st + 1], dq[b][4 * st + 2], dq[b][4 * st + 3]};
-        bf[b] = __builtin_bit_cast(bf16x8, v);
+        const uint32_t e = (ew[b] >> (8 * (st / 2))) & 0xffu;
+        u32x4 d;
+        if (fast) d = dequant8_fast(cw[b][st], e);
+        else d = dequant8_any(cw[b][st], e);
+        bf[b] = __builtin_bit_cast(bf16x8, d);
       }
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < NRT; ++rt) {
         const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[buf][rt * 32 + lc][32 * g + 8 * st]);
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[rt][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[b], acc[rt][b], 0, 0, 0);
@@ -277,19 +273,28 @@ __global__ __launch_bounds__(kPT) void grouped_gemm_kernel(PfArgs a) {
 
   // two register sets, two LDS buffers: step s uses set s % 2 and buffer s % 2. Writing
   // buffer s % 2 at step s is safe: every wave finished reading it (step s - 2) before the
-  // barrier of step s - 1.
-  // (K is a multiple of 2 kTK: the loop body is the same for every iteration)
-  StepRegs r0, r1;
-  load_step(r0, 0);
-  load_step(r1, kTK);
-  for (int k0 = 0; k0 < a.k; k0 += 2 * kTK) {
-    consume(r0, 0, k0 + 2 * kTK);
-    consume(r1, 1, k0 + 3 * kTK);
+  // barrier of step s - 1. K is a multiple of 2 kTK, so the loop body is the same for every
+  // iteration; one copy of the loop per count of row fragments.
+  auto run = [&](auto NC) __attribute__((always_inline)) {
+    StepRegs r0, r1;
+    load_step(r0, 0);
+    load_a(0);
+    load_step(r1, kTK);
+    for (int k0 = 0; k0 < a.k; k0 += 2 * kTK) {
+      consume(r0, 0, k0, NC);
+      consume(r1, 1, k0 + kTK, NC);
+    }
+  };
+  switch (nrt) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    default: run(std::integral_constant<int, 4>{}); break;
   }
 
   // epilogue: element i of a 32x32 tile sits at row (i/4)*8 + g*4 + i%4, column lc
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = rt * 32 + (i / 4) * 8 + g * 4 + (i % 4);

@@ -17,7 +17,9 @@
 #include "bfp_moe.hpp"
 
 // Many-token routing (prefill) is certified rather than computed in fp64 for every expert:
-//  1. approximate logits L~ = x . w_e on the bf16 matrix cores, fp32 accumulation. Every
+//  1. approximate logits L~ = x . w_e on the bf16 matrix cores, fp32 accumulation over up
+//     to four K slices whose partial sums are added in fp64 (a summation order like any other
+//     for the bound below, plus the rounding of that fp64 addition). Every
 //     product of two bf16 values is exact in fp32, so |L~ - L| <= gamma * sum_k |x_k w_k| with
 //     gamma = n u / (1 - n u), n = hidden, u = 2^-23 (any summation order, any rounding that is
 //     at least truncation), plus 2^-126 (|x|_1 + |w|_1) for products flushed as subnormals;
@@ -32,10 +34,51 @@ namespace bfp {
 
 namespace {
 
+// Cross-lane moves without LDS: DPP inside each 16-lane row (partners l^1, l^2, the mirror
+// inside the 8-lane half, l^8), then the four row results read back with v_readlane. Every
+// lane ends with the same value, combined in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true); }
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i32<CTRL>((int)(b & 0xffffffffll)), hi = dpp_i32<CTRL>((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<kDppQuadXor1>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppRowRor8>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// (value, index) pairs ordered by value descending, then index ascending
+__device__ __forceinline__ void better_of(double& bv, int& bi, double ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(double& bv, int& bi) {
+  better_of(bv, bi, dpp_f64<CTRL>(bv), dpp_i32<CTRL>(bi));
+}
+// wave-wide best (value, index); every lane gets the result
+__device__ __forceinline__ void wave_argmax(double& bv, int& bi) {
+  argmax_step<kDppQuadXor1>(bv, bi);
+  argmax_step<kDppQuadXor2>(bv, bi);
+  argmax_step<kDppHalfMirror>(bv, bi);
+  argmax_step<kDppRowRor8>(bv, bi);
+  double v = readlane_f64(bv, 0);
+  int i = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  for (int r = 1; r < 4; ++r) better_of(v, i, readlane_f64(bv, 16 * r), __builtin_amdgcn_readlane(bi, 16 * r));
+  bv = v;
+  bi = i;
 }
 
 // One wave per (token, 4 experts). Expert index n_exp is the shared-expert gate row.
@@ -102,12 +145,7 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
       if (ix[q] < a.n_exp && (v[q] > bv || (v[q] == bv && ix[q] < bi))) { bv = v[q]; bi = ix[q]; }
     }
     // wave argmax with the same order
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
+    wave_argmax(bv, bi);
     sel_l[j] = bv;
     sel_e[j] = bi;
 #pragma unroll
@@ -135,12 +173,16 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   }
 }
 
-// Counting sort of the (token, slot) pairs by expert; one workgroup of 1024 threads.
-// Tokens are processed in chunks of 1024 with a per-expert token bitmap in LDS: the rank of
-// a pair inside its expert is the number of earlier tokens in the bitmap row (prefix of
-// popcounts) plus the pairs of earlier chunks.
+// Counting sort of the (token, slot) pairs by expert; one workgroup of 1024 threads. The
+// expert ids are read from global memory once (16-byte loads, several in flight per thread)
+// into LDS as bytes; counts, scans, ranks and the stores then work from LDS. Tokens are ranked
+// in chunks of 1024 with a per-expert token bitmap: the rank of a pair inside its expert is
+// the number of earlier tokens in the bitmap row (prefix of popcounts) plus the pairs of
+// earlier chunks.
 constexpr int kDispThreads = 1024;
+constexpr int kDispMaxPairs = 8192 * 8;          // most tokens x top_k the kernel takes
 __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(DispatchArgs a) {
+  __shared__ uint8_t eid[kDispMaxPairs];
   __shared__ uint32_t bitmap[256][33];                      // 32 words + pad per expert
   __shared__ int cnt[256];
   __shared__ int off[257];
@@ -152,7 +194,33 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(DispatchArgs a) 
   if (tid < 256) { cnt[tid] = 0; base[tid] = 0; }
   __syncthreads();
   const int np = a.m * K;
-  for (int p = tid; p < np; p += kDispThreads) atomicAdd(&cnt[a.ids[p]], 1);
+  // ids -> LDS bytes and counts; four 16-byte loads issued before their use
+  const bool vec = (reinterpret_cast<uintptr_t>(a.ids) & 15) == 0;
+  const int nq = vec ? np / 4 : 0;
+  for (int q0 = tid; q0 < nq; q0 += 4 * kDispThreads) {
+    int4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + u * kDispThreads;
+      v[u] = q < nq ? reinterpret_cast<const int4*>(a.ids)[q] : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + u * kDispThreads;
+      if (q >= nq) continue;
+      const int e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        eid[4 * q + i] = (uint8_t)e4[i];
+        atomicAdd(&cnt[e4[i]], 1);
+      }
+    }
+  }
+  for (int p = 4 * nq + tid; p < np; p += kDispThreads) {
+    const int e = a.ids[p];
+    eid[p] = (uint8_t)e;
+    atomicAdd(&cnt[e], 1);
+  }
   __syncthreads();
   // exclusive scans over the experts (threads 0..255, one value each): pair offsets, the
   // rank of each active expert, and the first row tile of each active expert's group
@@ -203,10 +271,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(DispatchArgs a) 
     __syncthreads();
     const int t = c0 + tid;
     if (t < a.m)
-      for (int j = 0; j < K; ++j) {
-        const int e = a.ids[(int64_t)t * K + j];
-        atomicOr(&bitmap[e][tid / 32], 1u << (tid % 32));
-      }
+      for (int j = 0; j < K; ++j) atomicOr(&bitmap[eid[t * K + j]][tid / 32], 1u << (tid % 32));
     __syncthreads();
     {
       // 4 threads per expert, 8 bitmap words each; prefix over the 4 quarters by shuffles
@@ -229,7 +294,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(DispatchArgs a) 
     __syncthreads();
     if (t < a.m)
       for (int j = 0; j < K; ++j) {
-        const int e = a.ids[(int64_t)t * K + j];
+        const int e = eid[t * K + j];
         const int w = tid / 32, b = tid % 32;
         const int rank = base[e] + wpre[e][w] + __popc(bitmap[e][w] & ((1u << b) - 1u));
         const int pos = off[e] + rank;
@@ -249,15 +314,16 @@ constexpr int kRT = 64;           // tokens per router tile
 constexpr int kRE = 64;           // logit rows (experts) per router tile
 constexpr int kRK = 64;           // K per step
 constexpr int kRLDK = kRK + 8;
+constexpr int kRKS = 4;           // K slices of the many-token router (when hidden % 256 == 0)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 struct CertArgs {
   RouteArgs r;
-  float* approx;      // [m][ld_approx]
+  float* approx;      // [ks][m][ld_approx] partial logits, one plane per K slice
   int ld_approx;
-  double* norm_x;     // [m]
-  double* norm_w;     // [n_exp + 1]
+  int ks;             // K slices
+  double* norm2_w;    // [ks][n_exp + 1] partial squared norms of the logit rows
 };
 
 __device__ __forceinline__ const uint16_t* logit_row(const RouteArgs& a, int e) {
@@ -266,44 +332,22 @@ __device__ __forceinline__ const uint16_t* logit_row(const RouteArgs& a, int e) 
   return nullptr;
 }
 
-// Row norms in fp64: rows [0, m) are tokens, [m, m + n_exp + 1) are logit rows.
-__global__ __launch_bounds__(256) void row_norms_kernel(CertArgs c) {
-  const RouteArgs& a = c.r;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.m + a.n_exp + 1) return;
-  const uint16_t* p = row < a.m ? a.x + (int64_t)row * a.hidden : logit_row(a, row - a.m);
-  double s = 0.0;
-  if (p)
-    for (int cidx = lane; cidx < a.hidden / 8; cidx += 64) {
-      const uint4 v = *reinterpret_cast<const uint4*>(p + cidx * 8);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const double lo = bf16_lo(w4[i]), hi = bf16_hi(w4[i]);
-        s = __builtin_fma(lo, lo, s);
-        s = __builtin_fma(hi, hi, s);
-      }
-    }
-  s = wave_sum_f64(s);
-  if (lane == 0) {
-    // a slightly enlarged norm keeps the bound an upper bound despite fp64 rounding
-    const double nrm = sqrt(s) * (1.0 + 1e-12);
-    if (row < a.m) c.norm_x[row] = nrm; else c.norm_w[row - a.m] = nrm;
-  }
-}
-
-// Approximate logits on the bf16 matrix cores: a 64-token x 64-row tile per workgroup.
+// Approximate logits on the bf16 matrix cores: a 64-token x 64-row tile over one K slice per
+// workgroup (grid z = slice). Workgroups of the first token tile also accumulate the squared
+// norms of their 64 logit rows over the slice, in fp64.
 __global__ __launch_bounds__(256) void router_mfma_kernel(CertArgs c) {
   const RouteArgs& a = c.r;
   __shared__ __align__(16) uint16_t As[kRT][kRLDK];
   __shared__ __align__(16) uint16_t Bs[kRE][kRLDK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRE;
+  const int kslice = a.hidden / c.ks, kbeg = blockIdx.z * kslice;
   const int r = tid / 4, q = tid % 4;            // 64 rows x 4 quarters of 16 values
   const int tok = t0 + r;
   const uint16_t* arow = tok < a.m ? a.x + (int64_t)tok * a.hidden : nullptr;
   const uint16_t* brow = logit_row(a, e0 + r);
+  const bool norms = blockIdx.x == 0;
+  double nw2 = 0.0;
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -315,16 +359,28 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(CertArgs c) {
       rb[h] = brow ? *reinterpret_cast<const uint4*>(brow + k0 + q * 16 + h * 8) : make_uint4(0, 0, 0, 0);
     }
   };
-  load(0);
-  for (int k0 = 0; k0 < a.hidden; k0 += kRK) {
+  load(kbeg);
+  for (int k0 = kbeg; k0 < kbeg + kslice; k0 += kRK) {
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       *reinterpret_cast<uint4*>(&As[r][q * 16 + h * 8]) = ra[h];
       *reinterpret_cast<uint4*>(&Bs[r][q * 16 + h * 8]) = rb[h];
     }
+    if (norms) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w4[4] = {rb[h].x, rb[h].y, rb[h].z, rb[h].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const double lo = bf16_lo(w4[i]), hi = bf16_hi(w4[i]);
+          nw2 = __builtin_fma(lo, lo, nw2);
+          nw2 = __builtin_fma(hi, hi, nw2);
+        }
+      }
+    }
     __syncthreads();
-    if (k0 + kRK < a.hidden) load(k0 + kRK);
+    if (k0 + kRK < kbeg + kslice) load(k0 + kRK);
 #pragma unroll
     for (int ks = 0; ks < kRK / 32; ++ks) {
       const int kk = ks * 32 + 8 * (lane / 16);
@@ -336,6 +392,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(CertArgs c) {
       }
     }
   }
+  float* out = c.approx + (int64_t)blockIdx.z * a.m * c.ld_approx;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tt = t0 + wave * 16 + 4 * (lane / 16) + i;
@@ -343,25 +400,52 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(CertArgs c) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + j * 16 + (lane % 16);
-      if (e <= a.n_exp) c.approx[(int64_t)tt * c.ld_approx + e] = acc[j][i];
+      if (e <= a.n_exp) out[(int64_t)tt * c.ld_approx + e] = acc[j][i];
     }
+  }
+  if (norms) {
+    // the 4 quarters of a row are adjacent lanes
+    nw2 += __shfl_xor(nw2, 1);
+    nw2 += __shfl_xor(nw2, 2);
+    if (q == 0 && e0 + r <= a.n_exp) c.norm2_w[(int64_t)blockIdx.z * (a.n_exp + 1) + e0 + r] = nw2;
   }
 }
 
-// exact fp64 logit of one row (wave-wide)
-__device__ __forceinline__ double exact_logit(const uint16_t* x, const uint16_t* w, int hidden, int lane) {
-  double s = 0.0;
-  for (int cidx = lane; cidx < hidden / 8; cidx += 64) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(x + cidx * 8);
-    const uint4 wv = *reinterpret_cast<const uint4*>(w + cidx * 8);
-    const uint32_t xa[4] = {xv.x, xv.y, xv.z, xv.w}, wa[4] = {wv.x, wv.y, wv.z, wv.w};
+// Exact fp64 logits of NR rows against one token row (wave-wide). Each pass covers up to four
+// 8-value chunks per lane of x and of every row, all loaded before any arithmetic.
+template <int NR>
+__device__ __forceinline__ void exact_logits(const uint16_t* x, const uint16_t* const* w, int hidden, int lane,
+                                             double* out) {
+  double s[NR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s = __builtin_fma((double)bf16_lo(xa[i]), (double)bf16_lo(wa[i]), s);
-      s = __builtin_fma((double)bf16_hi(xa[i]), (double)bf16_hi(wa[i]), s);
+  for (int i = 0; i < NR; ++i) s[i] = 0.0;
+  const int chunks = hidden / 8;
+  for (int c0 = 0; c0 < chunks; c0 += 4 * 64) {
+    uint4 xv[4], wv[NR][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * 64 + lane;
+      const bool ok = c < chunks;
+      xv[u] = ok ? *reinterpret_cast<const uint4*>(x + c * 8) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) wv[i][u] = ok ? *reinterpret_cast<const uint4*>(w[i] + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t xa[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const uint32_t wa[4] = {wv[i][u].x, wv[i][u].y, wv[i][u].z, wv[i][u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[i] = __builtin_fma((double)bf16_lo(xa[j]), (double)bf16_lo(wa[j]), s[i]);
+          s[i] = __builtin_fma((double)bf16_hi(xa[j]), (double)bf16_hi(wa[j]), s[i]);
+        }
+      }
     }
   }
-  return wave_sum_f64(s);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) out[i] = wave_sum_f64(s[i]);
 }
 
 // One wave per token: certify the candidate set, recompute its logits exactly, select.
@@ -377,18 +461,47 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
   const double u = 1.0 / 8388608.0;                       // 2^-23
   const double gamma = n * u / (1.0 - n * u);
   const double tiny = 1.1754943508222875e-38;             // 2^-126
-  const double nx = c.norm_x[t];
+  // |x|_2 of this token (fp64, slightly enlarged so that the bound stays an upper bound)
+  double sx = 0.0;
+  for (int c0 = 0; c0 < a.hidden / 8; c0 += 4 * 64) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cidx = c0 + u * 64 + lane;
+      v[u] = cidx < a.hidden / 8 ? *reinterpret_cast<const uint4*>(xr + cidx * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double l = bf16_lo(w4[i]), h = bf16_hi(w4[i]);
+        sx = __builtin_fma(l, l, sx);
+        sx = __builtin_fma(h, h, sx);
+      }
+    }
+  }
+  const double nx = sqrt(wave_sum_f64(sx)) * (1.0 + 1e-12);
   double lo[4], hi[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
     if (e < a.n_exp) {
-      const double nw = c.norm_w[e];
-      const double d = gamma * nx * nw + tiny * sqrt(n) * (nx + nw) * 1.01;
+      double nw2 = 0.0, v = 0.0, av = 0.0;
+#pragma unroll 4
+      for (int z = 0; z < c.ks; ++z) {
+        nw2 += c.norm2_w[(int64_t)z * (a.n_exp + 1) + e];
+        const double p = (double)c.approx[((int64_t)z * a.m + t) * c.ld_approx + e];
+        v += p;
+        av += __builtin_fabs(p);
+      }
+      const double nw = sqrt(nw2) * (1.0 + 1e-12);
+      // fp32 sums inside the slices: gamma |x| |w| (any summation order); the slices are added
+      // in fp64 (1e-15 of their magnitudes covers that rounding)
+      const double d = gamma * nx * nw + tiny * sqrt(n) * (nx + nw) * 1.01 + 1e-15 * av;
       const double b = a.bias ? (double)a.bias[e] : 0.0;
-      const double v = (double)c.approx[(int64_t)t * c.ld_approx + e] + b;
-      lo[q] = v - d;
-      hi[q] = v + d;
+      lo[q] = v + b - d;
+      hi[q] = v + b + d;
     } else {
       lo[q] = -__builtin_huge_val();
       hi[q] = -__builtin_huge_val();
@@ -405,12 +518,7 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
       for (int q = 0; q < 4; ++q) if (v[q] > bv) { bv = v[q]; bq = q; }
       double mv = bv;
       int ml = lane;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const double ov = __shfl_xor(mv, o);
-        const int ol = __shfl_xor(ml, o);
-        if (ov > mv || (ov == mv && ol < ml)) { mv = ov; ml = ol; }
-      }
+      wave_argmax(mv, ml);
       lk = mv;
       if (lane == ml && bq >= 0) v[bq] = -__builtin_huge_val();
     }
@@ -428,14 +536,27 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
     nc += __popcll(bal);
   }
   __builtin_amdgcn_wave_barrier();
-  // exact logits of the candidates
-  for (int i = 0; i < nc; ++i) {
-    const int e = cand[wv][i];
-    const double s = exact_logit(xr, a.router_w + (int64_t)e * a.hidden, a.hidden, lane);
-    if (lane == 0) cval[wv][i] = s + (a.bias ? (double)a.bias[e] : 0.0);
+  // exact logits of the candidates, four rows per pass
+  for (int i0 = 0; i0 < nc; i0 += 4) {
+    const uint16_t* rows[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rows[i] = a.router_w + (int64_t)cand[wv][min(i0 + i, nc - 1)] * a.hidden;
+    double ex4[4];
+    exact_logits<4>(xr, rows, a.hidden, lane, ex4);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i0 + i < nc) {
+          const int e = cand[wv][i0 + i];
+          cval[wv][i0 + i] = ex4[i] + (a.bias ? (double)a.bias[e] : 0.0);
+        }
+    }
   }
   double glog = 0.0;
-  if (a.sh_gate_w) glog = exact_logit(xr, a.sh_gate_w, a.hidden, lane);
+  if (a.sh_gate_w) {
+    const uint16_t* rows[1] = {a.sh_gate_w};
+    exact_logits<1>(xr, rows, a.hidden, lane, &glog);
+  }
   __builtin_amdgcn_wave_barrier();
   // top-k among the candidates by (exact logit desc, expert asc)
   double v[4];
@@ -454,12 +575,7 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (ix[q] != 0x7fffffff && (v[q] > bv || (v[q] == bv && ix[q] < bi))) { bv = v[q]; bi = ix[q]; }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
+    wave_argmax(bv, bi);
     sel_l[j] = bv;
     sel_e[j] = bi;
 #pragma unroll
@@ -486,26 +602,25 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
 size_t route_workspace_bytes(int m, int n_exp) {
   const size_t fp64 = (size_t)m * (n_exp + 1) * sizeof(double);
   const int ld = (n_exp + 1 + kRE - 1) / kRE * kRE;
-  const size_t cert = (size_t)m * ld * sizeof(float) + (size_t)m * sizeof(double) + (size_t)(n_exp + 1) * sizeof(double) + 64;
+  const size_t cert = (size_t)kRKS * m * ld * sizeof(float) + (size_t)kRKS * (n_exp + 1) * sizeof(double) + 64;
   return fp64 > cert ? fp64 : cert;
 }
 
 hipError_t router_launch(const RouteArgs& a, hipStream_t s) {
   if (a.m > 32) {
-    // certified many-token routing; the logits region holds approx, then the two norm arrays
+    // certified many-token routing; the logits region holds the partial logits, then the
+    // partial squared norms of the logit rows
     CertArgs c;
     c.r = a;
+    c.ks = a.hidden % (kRKS * kRK) == 0 ? kRKS : 1;
     c.ld_approx = (a.n_exp + 1 + kRE - 1) / kRE * kRE;
     c.approx = reinterpret_cast<float*>(a.logits);
-    char* base = reinterpret_cast<char*>(a.logits) + (size_t)a.m * c.ld_approx * sizeof(float);
-    c.norm_x = reinterpret_cast<double*>(base);
-    c.norm_w = c.norm_x + a.m;
-    hipLaunchKernelGGL(row_norms_kernel, dim3((a.m + a.n_exp + 1 + 3) / 4), dim3(256), 0, s, c);
+    char* base = reinterpret_cast<char*>(a.logits) + (size_t)kRKS * a.m * c.ld_approx * sizeof(float);
+    c.norm2_w = reinterpret_cast<double*>(base);
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((a.m + kRT - 1) / kRT, (a.n_exp + 1 + kRE - 1) / kRE, c.ks),
+                       dim3(256), 0, s, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((a.m + kRT - 1) / kRT, (a.n_exp + 1 + kRE - 1) / kRE), dim3(256), 0,
-                       s, c);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(certify_topk_kernel, dim3((a.m + 3) / 4), dim3(256), 0, s, c);
     return hipGetLastError();
   }
