@@ -80,9 +80,8 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemv_kernel(MoeGemvArgs ma, i
   }
 }
 
-template <int NMAT, bool XB, int MBMAX>
-hipError_t launch_mbmax(const MoeGemvArgs& ma, hipStream_t s) {
-  constexpr int LPR = 16;
+template <int NMAT, bool XB, int MBMAX, int LPR>
+hipError_t launch_lpr(const MoeGemvArgs& ma, hipStream_t s) {
   using L = XLayout<XB, 32>;
   const int kc = pick_kc(ma.k, MBMAX, 32, LPR, L::kBytesPerValue);
   const size_t lds = (size_t)MBMAX * (kc / 32) * L::kStrideDw * sizeof(uint32_t);
@@ -93,6 +92,17 @@ hipError_t launch_mbmax(const MoeGemvArgs& ma, hipStream_t s) {
   dim3 grid((ma.rows_per_expert + RPW - 1) / RPW, groups);
   hipLaunchKernelGGL((moe_gemv_kernel<NMAT, XB, MBMAX, LPR>), grid, dim3(kMoeThreads), lds, s, ma, kc);
   return hipGetLastError();
+}
+
+// Lanes per row from K alone: about four 32-value units per lane (4 to 16 lanes), so that
+// short rows (the down projection) still give every lane several loads and a workgroup many
+// rows.
+template <int NMAT, bool XB, int MBMAX>
+hipError_t launch_mbmax(const MoeGemvArgs& ma, hipStream_t s) {
+  const int units = ma.k / 32;
+  if (units <= 16) return launch_lpr<NMAT, XB, MBMAX, 4>(ma, s);
+  if (units <= 32) return launch_lpr<NMAT, XB, MBMAX, 8>(ma, s);
+  return launch_lpr<NMAT, XB, MBMAX, 16>(ma, s);
 }
 
 template <int NMAT, bool XB>
