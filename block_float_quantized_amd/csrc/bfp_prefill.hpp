@@ -24,11 +24,15 @@ struct PrefillArgs {
   const int32_t* n_active;    // [1]
   uint16_t* h;                // bf16 [m*top_k + m][inter]
   float* o;                   // fp32 [m*top_k + m][hidden]
-  const int32_t* tile_start;  // row-tile list written by the dispatch kernel (tile_m rows)
+  int32_t* extra;             // the region sized by prefill_workspace_extra_bytes: first the
+                              // per-group row-tile starts the dispatch kernel writes (tile_m
+                              // rows), then scratch of the prefill kernels
 };
 
-// Bytes of the tile list, and the row-tile height the dispatch kernel must use for it.
-size_t prefill_workspace_extra_bytes(int m, int n_exp, int top_k);
+// Bytes of the region after the pair buffers: the dispatch kernel's row-tile starts, the row
+// tiles sorted by size, and x permuted to the weight unpack's pair order; and the row-tile
+// height the dispatch kernel must use.
+size_t prefill_workspace_extra_bytes(int m, int n_exp, int top_k, int hidden);
 int prefill_tile_rows();
 hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s);
 

@@ -76,7 +76,7 @@ Layout layout(const bfp_moe_layer* L, int64_t m, bool with_experts) {
       y.h = place(off, (size_t)pairs * F * 2);       // bf16 h
       y.o = place(off, (size_t)pairs * H * 4);
       y.extra = off;
-      y.total = off + bfp::prefill_workspace_extra_bytes((int)m, (int)E, (int)K);
+      y.total = off + bfp::prefill_workspace_extra_bytes((int)m, (int)E, (int)K, (int)H);
       return y;
     }
     y.h = place(off, (size_t)pairs * F * 4);
@@ -181,7 +181,7 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
     p.w = w; p.g = shared ? g : nullptr; p.inv = d.inv; p.perm = d.perm; p.offsets = d.offsets;
     p.counts = d.counts; p.active = d.active; p.n_active = d.n_active;
     p.h = at<uint16_t>(ws, ly.h); p.o = at<float>(ws, ly.o);
-    p.tile_start = d.tile_start;
+    p.extra = d.tile_start;
     return from_hip(bfp::prefill_launch(p, s));
   }
 

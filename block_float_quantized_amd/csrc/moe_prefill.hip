@@ -10,18 +10,21 @@
 // of each token's pair rows (the decode combine kernel).
 //
 // Kernel design:
-//  * One workgroup (4 waves) computes a TM x TN tile of one group. The tile list (row tiles
-//    of every group) comes from the dispatch kernel; workgroups are mapped so that each XCD
-//    takes a contiguous range of tiles, ordered (group, column tile, row tile): the tiles
-//    that reuse one expert's weights share an L2.
-//  * Per K step of 64: the activation rows are gathered (token rows of x, or pair rows of h)
-//    into LDS; each lane loads and dequantizes its own weight values straight into MFMA B
-//    operands (the weights never go through LDS); the next step's global loads are issued
-//    before the current step's MFMAs.
-//  * v_mfma_f32_32x32x16_bf16 with fp32 accumulation; each wave owns all 64 rows of the tile
-//    and 64 output columns.
+//  * One workgroup (4 waves, two workgroups per CU) computes a 128-row x TN tile of one
+//    group. The row tiles of every group come from the dispatch kernel; a small pass sorts
+//    them heaviest first (row fragments that hold rows), and workgroup j takes column tile
+//    j % nct of sorted row tile j / nct, so that the long tiles start first.
+//  * Every operand reaches LDS by buffer loads that write LDS directly (no registers, no
+//    waits in the issuing wave): activation rows per K step of 64 (three steps in flight),
+//    weight codes per block of two steps with 4 lanes per column (every load instruction
+//    touches 16 lines and uses 64 bytes of each), the block exponents into registers. One
+//    barrier per step; the waits for the loads are counted by hand, since the compiler
+//    cannot see which LDS range a load fills.
+//  * v_mfma_f32_32x32x16_bf16 with fp32 accumulation; each wave owns all 128 rows of the
+//    tile and 64 output columns.
 //    A and B share one permutation of K inside every 8-value group (the order the BFP4
-//    unpack produces pairs in), which leaves every dot product unchanged.
+//    unpack produces pairs in), which leaves every dot product unchanged: x is permuted once
+//    before the gate/up GEMM, and h is written permuted by its epilogue.
 //  * Dequantization is exact: a nibble becomes an FP8 E4M3 subnormal (mag * 2^-9) and the
 //    conversion to bf16 applies the block scale 2^(E-120); blocks whose scale falls outside
 //    the conversion's exact range go through an fp32 path.
@@ -40,8 +43,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kTM = 128;         // rows (pairs) per tile
 constexpr int kRT = kTM / 32;    // 32-row MFMA fragments per tile
 constexpr int kTK = 64;          // K per step
-constexpr int kLDK = kTK + 8;    // bf16 per LDS row (padding spreads banks)
-constexpr int kPT = 256;         // threads per workgroup
+constexpr int kPT = 256;         // threads per workgroup (two workgroups per CU)
+constexpr int kWaves = kPT / 64;
+constexpr int kNB = 2;           // 32-column B tiles per wave
+constexpr int kWaveCols = 32 * kNB;
+constexpr int kStagesA = 3;      // activation steps in the LDS ring
+constexpr int kAStageBytes = kTM * kTK * 2;
+constexpr int kBBlk = 2;         // K steps per weight-code block
+constexpr int kBRing = 2;        // weight-code blocks in the LDS ring
+constexpr int kBColBytes = kTK * kBBlk / 2;             // code bytes of one column per block
+constexpr int kBWaveBytes = kWaveCols * kBColBytes;
+constexpr int kBBlockBytes = kWaves * kBWaveBytes;
 
 struct PfArgs {
   const uint8_t *exp0, *code0, *exp1, *code1;       // routed (stacked) matrices
@@ -53,10 +65,12 @@ struct PfArgs {
   const int32_t* offsets;
   const int32_t* perm;
   const int32_t* tile_start;
+  const int32_t* items;                             // row tiles, heaviest first: group << 16 | tile
   int with_shared;
   int m, top_k;
   const uint16_t* a;                                // A rows (bf16): x by token, or h by position
   int64_t lda;
+  uint32_t a_bytes;                                 // bytes of A (below 2 GiB)
   int a_by_token;
   void* c;                                          // output rows by pair position
   int64_t ldc;
@@ -104,29 +118,19 @@ struct TileInfo {
   int col0;         // first output column
 };
 
-// Maps this workgroup to a tile; false when it has none. Each XCD (workgroups bid % 8) takes a
-// contiguous range of the tiles that exist.
+// Maps this workgroup to a tile; false when it has none. Workgroup j takes column tile j % nct
+// of row tile j / nct in the sorted list: the heaviest tiles start first (list scheduling,
+// longest first, as workgroups are dispatched in index order), and the XCDs (workgroups j % 8)
+// each get a share of every class.
 template <int TN>
 __device__ __forceinline__ bool find_tile(const PfArgs& a, TileInfo& t) {
   const int na = *a.n_active;
   const int ng = na + (a.with_shared ? 1 : 0);
-  const int nct = a.rows_per_expert / TN;
-  const int total = a.tile_start[ng] * nct;
-  const int per = (total + 7) / 8;
-  const int local = blockIdx.x / 8;
-  if (local >= per) return false;
-  const int tile = (blockIdx.x % 8) * per + local;
-  if (tile >= total) return false;
-  // group: last g with tile_start[g] * nct <= tile
-  int lo = 0, hi = ng - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (a.tile_start[mid] * nct <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int g = lo;
-  const int mtiles = a.tile_start[g + 1] - a.tile_start[g];
-  const int loc = tile - a.tile_start[g] * nct;
-  const int ct = loc / mtiles, mt = loc % mtiles;
+  const int nct = (a.rows_per_expert + TN - 1) / TN;
+  const int j = blockIdx.x;
+  if (j >= a.tile_start[ng] * nct) return false;
+  const int item = a.items[j / nct];
+  const int g = item >> 16, mt = item & 0xffff, ct = j % nct;
   t.shared = g == na;
   if (t.shared) {
     t.e = -1;
@@ -146,143 +150,257 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Grouped GEMM C[pos][col] = A[row(pos)] . W_e[col] for one tile of kTM rows, on
 // v_mfma_f32_32x32x16_bf16. Each of the 4 waves owns all kTM rows (kRT 32-row A fragments)
-// and NB = 2 B tiles of 32 columns: NMAT = 2 -> the same 32 columns of gate and of up (the
+// and kNB = 2 B tiles of 32 columns: NMAT = 2 -> the same 32 columns of gate and of up (the
 // SwiGLU pair lands in one lane), NMAT = 1 -> 64 adjacent columns. A workgroup therefore
-// covers TN = 4 * 32 * 2 / NMAT columns of each matrix.
+// covers TN = 4 * 64 / NMAT columns of each matrix (two workgroups per CU: the LDS rings
+// below take 80 KB each).
 //
-// Per K step of 64: the gathered A rows go through LDS (shared by the 4 waves); every lane
-// loads the 16 code bytes (32 values) of each of its B rows directly and dequantizes them
-// in registers, so the weights never touch LDS. Lane group g = lane / 32 takes K values
-// [32g, 32g + 32) of the step, 8 per MFMA; its A fragment reads the same K values from LDS.
+// Every operand goes through LDS, loaded by buffer loads straight into LDS (no registers):
+//  * activations, per K step of 64: kTM rows of 128 bytes, gathered by row, in a ring of
+//    kStagesA steps;
+//  * weight codes, per block of kBBlk steps: each wave's 64 columns x 64 bytes, in a ring of
+//    kBRing blocks. A load instruction covers 16 columns with 4 lanes each, so it touches 16
+//    lines and uses 64 bytes of each (with one lane per column, 32 lines and 32 bytes);
+//  * the block exponents go to registers, 16 bytes per column per 4 steps.
+// Lane group g = lane / 32 takes K values [32g, 32g + 32) of a step, 8 per MFMA; its A
+// fragment reads the same K values. Both operand reads use XOR-swizzled 16-byte slots, so
+// the 8 lanes a read serves at once hit distinct banks.
+
+// Wait until at most N of this wave's LDS reads are outstanding, then redefine the NR
+// fragments (an empty statement that claims to write them), so that nothing reading them
+// can be scheduled before the wait.
+template <int N, int NR>
+__device__ __forceinline__ void wait_lds(u32x4* r) {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+#pragma unroll
+  for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+// A pointer every lane holds the same value of, moved to scalar registers.
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt vmcnt(n), every other counter left alone
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xF) | (N & 0xF) | ((N >> 4) << 14));
+}
+
+// keeps the compiler from moving memory accesses across this point
+__device__ __forceinline__ void mem_order() { asm volatile("" ::: "memory"); }
+
 template <int NMAT>
 __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
-  constexpr int NB = 2;                            // 32-column B tiles per wave
-  constexpr int TN = 4 * 32 * NB / NMAT;           // columns per matrix per workgroup
-  __shared__ __align__(16) uint16_t As[2][kTM][kLDK];
-  __shared__ int arow[kTM];
+  constexpr int TN = kWaves * kWaveCols / NMAT;   // columns per matrix per workgroup
+  __shared__ __align__(16) uint8_t As[kStagesA][kAStageBytes];
+  __shared__ __align__(16) uint8_t Bs[kBRing][kBBlockBytes];
   TileInfo t;
   if (!find_tile<TN>(a, t)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane / 32, lc = lane % 32;
-  if (tid < kTM) {
-    const int r = t.row0 + tid;
-    int row = -1;
-    if (r < t.n) {
-      const int pos = t.p0 + r;
-      const int tok = t.shared ? r : a.perm[pos] / a.top_k;
-      row = a.a_by_token ? tok : pos;
-    }
-    arow[tid] = row;
-  }
-  __syncthreads();
+  // A row (token row of x, or pair row of h) of tile row rr; rows past the group read the
+  // group's first row: their results are never stored
+  auto arow = [&](int rr) {
+    const int r = t.row0 + rr < t.n ? t.row0 + rr : t.row0;
+    const int pos = t.p0 + r;
+    const int tok = t.shared ? r : a.perm[pos] / a.top_k;
+    return a.a_by_token ? tok : pos;
+  };
 
-  const int64_t nbk = a.k / kBlock;
+  const int nbk = a.k / kBlock;
   const int64_t rows0 = t.shared ? 0 : (int64_t)t.e * a.rows_per_expert;
   const uint8_t* expb[2] = {(t.shared ? a.sexp0 : a.exp0) + rows0 * nbk,
                             NMAT == 2 ? (t.shared ? a.sexp1 : a.exp1) + rows0 * nbk : nullptr};
   const uint8_t* codeb[2] = {(t.shared ? a.scode0 : a.code0) + rows0 * (a.k / 2),
                              NMAT == 2 ? (t.shared ? a.scode1 : a.code1) + rows0 * (a.k / 2) : nullptr};
-  // B row (output column) of tile b of this lane, and the matrix it belongs to
-  const uint8_t* bcode[NB];
-  const uint8_t* bexp[NB];
+  // one buffer descriptor per matrix over this group's rows: loads past them (columns past
+  // N in the last column tile) return zeros
+  // (named descriptors, not an array: the host pass rejects array elements as operands of
+  // the load-to-LDS builtin and silently drops the kernel)
+  const int cbytes = a.rows_per_expert * (a.k / 2), ebytes = a.rows_per_expert * nbk;
+  const __amdgpu_buffer_rsrc_t crs0 = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(codeb[0]), (short)0, cbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t crs1 = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(codeb[NMAT - 1]), (short)0, cbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ers0 = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(expb[0]), (short)0, ebytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ers1 = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(expb[NMAT - 1]), (short)0, ebytes, 0x00020000);
+  // this wave's weight rows c = 0..63: matrix and output column
+  auto wcol = [&](int c) { return NMAT == 2 ? t.col0 + 32 * wave + c % 32 : t.col0 + 64 * wave + c; };
+
+  // activation loads: 16 instructions per step, 4 per wave, each filling 8 rows (1 KB);
+  // lane i brings 16 bytes of row 8 (4 wave + q) + i / 8, source chunk (i % 8) ^ (row % 8),
+  // to byte 16 i of the instruction's 1 KB (the activations are stored pre-permuted)
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a.a, (short)0, (int)a.a_bytes, 0x00020000);
+  constexpr int kAQ = kTM / 8 / kWaves;  // activation instructions per wave and step
+  uint32_t asrc[kAQ];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int mat = NMAT == 2 ? b : 0;
-    const int col = NMAT == 2 ? t.col0 + wave * 32 + lc : t.col0 + wave * 64 + b * 32 + lc;
-    bcode[b] = codeb[mat] + (int64_t)col * (a.k / 2);
-    bexp[b] = expb[mat] + (int64_t)col * nbk;
+  for (int q = 0; q < kAQ; ++q) {
+    const int rr = 8 * (kAQ * wave + q) + lane / 8;
+    const int chunk = (lane % 8) ^ (rr % 8);
+    asrc[q] = (uint32_t)(((int64_t)arow(rr) * a.lda + chunk * 8) * 2);
   }
-  // A staging: kTM rows x 64 values = 256 threads x 32 values
-  constexpr int kAQ = kPT / kTM;                   // threads per row
-  constexpr int kAH = 64 / kAQ / 8;                // 8-value pieces per thread
-  const int ar = tid / kAQ, aq = tid % kAQ;
-  const int arow_this = arow[ar];
+  auto load_a = [&](int stage, int step) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < kAQ; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (__attribute__((address_space(3))) void*)&As[stage][(kAQ * wave + q) * 1024], 16,
+                                               asrc[q], step * kTK * 2, 0, 0);
+  };
+  // weight-code loads: 4 instructions per block, instruction q covering this wave's columns
+  // c = 16 q + 2 p + u / 4 (p = lane / 8, u = lane % 8); the lane brings 16-byte chunk
+  // (u % 4) ^ (p % 4) of the column's 64-byte block to byte 16 lane of the instruction's 1 KB,
+  // so that chunk j of column c sits at byte (c / 2) 128 + ((c % 2) 4 + (j ^ (c / 2) % 4)) 16
+  uint32_t bsrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = 16 * q + 2 * (lane / 8) + (lane % 8) / 4;
+    const int j = (lane % 4) ^ ((lane / 8) % 4);
+    bsrc[q] = (uint32_t)(wcol(c) * (a.k / 2) + 16 * j);
+  }
+  auto load_b = [&](int slot, int blk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 ? crs0 : crs1,
+                                               (__attribute__((address_space(3))) void*)&Bs[slot][wave * kBWaveBytes + q * 1024], 16,
+                                               bsrc[q], blk * kBColBytes, 0, 0);
+  };
+  // exponent loads: per B tile, the 16 bytes of this lane's column covering 4 steps
+  uint32_t eoff[kNB];
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) eoff[b] = (uint32_t)(wcol(b * 32 + lc) * nbk);
+  auto load_e = [&](u32x4* E, int grp) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) E[b] = __builtin_amdgcn_raw_buffer_load_b128(b == 0 ? ers0 : ers1, eoff[b], grp * 16, 0);
+  };
+
+  // LDS byte addresses: A row lc of stage 0 with its swizzle, and the code slots of this
+  // lane's two columns b * 32 + lc in wave block 0
+  const uint32_t lds_a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&As[0][0] + (uint32_t)(lc * kTK * 2);
+  const uint32_t a_g4 = (uint32_t)(4 * g), a_sw = (uint32_t)(lc % 8);
+  const uint32_t lds_b = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&Bs[0][0] +
+                         (uint32_t)(wave * kBWaveBytes + (lc / 2) * 128 + (lc % 2) * 64);
+  const uint32_t b_sw = (uint32_t)((lc / 2) % 4);
+
   // rows of this tile that exist (wave-uniform): MFMAs of fragments past them are skipped
   const int nrt = (min(kTM, t.n - t.row0) + 31) / 32;
+  const int nsteps = a.k / kTK;          // even
+  const int nblk = nsteps / kBBlk;
+  const int ngrp = (nsteps + 3) / 4;
 
-  // weight loads of one K step (issued two steps ahead), kept in registers until consumed;
-  // activation loads of the next step (one step ahead) go to one register set
-  struct StepRegs {
-    u32x4 rc[NB];
-    uint32_t re[NB];
-  };
-  auto load_step = [&](StepRegs& R, int k0) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      R.rc[b] = *reinterpret_cast<const u32x4*>(bcode[b] + (k0 + 32 * g) / 2);
-      R.re[b] = *reinterpret_cast<const uint16_t*>(bexp[b] + (k0 + 32 * g) / 16);
-    }
-  };
-  uint4 ra[kAH];
-  auto load_a = [&](int k0) {
-#pragma unroll
-    for (int h = 0; h < kAH; ++h) {
-      ra[h] = make_uint4(0, 0, 0, 0);
-      if (arow_this >= 0)
-        ra[h] = *reinterpret_cast<const uint4*>(a.a + (int64_t)arow_this * a.lda + k0 + aq * 8 * kAH + h * 8);
-    }
-  };
-
-  f32x16 acc[kRT][NB];
+  f32x16 acc[kRT][kNB];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[rt][b] = f32x16{};
+    for (int b = 0; b < kNB; ++b) acc[rt][b] = f32x16{};
 
-  // consume step k0: stage its activations into LDS buffer `buf`, one barrier, then issue the
-  // loads of the next step's activations and of the weights two steps ahead, then dequantize
-  // and run the MFMAs of the NRT fragments that hold rows
-  auto consume = [&](StepRegs& R, int buf, int k0, auto NC) __attribute__((always_inline)) {
+  // Step s (SP = s % 4): wait until this wave's loads of step s have landed, one barrier
+  // (every wave's have; every wave is done with the slots refilled next), issue the
+  // activations of step s + 2, on even steps the weight block of steps s + 2 and s + 3, on
+  // SP = 0 the exponents of steps s + 4 .. s + 7, then compute. Loads past the end repeat
+  // the last step, block or group, so every step issues the same loads. Per wave a step
+  // issues 4 activation loads, 4 weight loads on even steps and 2 exponent loads on SP = 0,
+  // in that order; counting those issued after the ones step s needs (its activations,
+  // issued two steps earlier, and on even steps its weight block, issued right after them)
+  // gives the wait below.
+  u32x4 ecur[kNB], enext[kNB];
+  auto step = [&](int s, auto SPC, auto NC) __attribute__((always_inline)) {
+    constexpr int SP = decltype(SPC)::value;
     constexpr int NRT = decltype(NC)::value;
-    // one decision per wave and step: all exponents inside the fast conversion's range?
+    wait_vm<SP == 0 ? 4 : SP == 1 ? 10 : SP == 2 ? 6 : 8>();
+    mem_order();
+    __builtin_amdgcn_s_barrier();
+    mem_order();
+    load_a((s + 2) % kStagesA, min(s + 2, nsteps - 1));
+    mem_order();
+    if constexpr (SP % 2 == 0) {
+      load_b((s / 2 + 1) % kBRing, min(s / 2 + 1, nblk - 1));
+      mem_order();
+    }
+    if constexpr (SP == 0) {
+      load_e(enext, min(s / 4 + 1, ngrp - 1));
+      mem_order();
+    }
+    // this step's code chunks (16 bytes = 32 values per column) and exponents
+    const uint32_t bj = (uint32_t)(2 * (SP % 2) + g);
+    const uint32_t bb = lds_b + (uint32_t)(((s / 2) % kBRing) * kBBlockBytes) + ((bj ^ b_sw) << 4);
+    u32x4 cw[kNB];
+    static_assert(kNB == 2 && 16 * 128 == 2048, "tile stride");
+    asm volatile("ds_read_b128 %0, %1" : "=v"(cw[0]) : "v"(bb));
+    asm volatile("ds_read_b128 %0, %1 offset:2048" : "=v"(cw[1]) : "v"(bb));
+    uint32_t ew[kNB];
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) ew[b] = (ecur[b][SP] >> (16 * g)) & 0xffffu;
     bool ok = true;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) ok = ok && ((R.re[b] & 0xffu) - 8u) <= 239u && ((R.re[b] >> 8) - 8u) <= 239u;
+    for (int b = 0; b < kNB; ++b) ok = ok && ((ew[b] & 0xffu) - 8u) <= 239u && ((ew[b] >> 8) - 8u) <= 239u;
     const bool fast = __builtin_amdgcn_ballot_w64(!ok) == 0;
-#pragma unroll
-    for (int h = 0; h < kAH; ++h) *reinterpret_cast<uint4*>(&As[buf][ar][aq * 8 * kAH + h * 8]) = permute8(ra[h]);
-    u32x4 cw[NB];
-    uint32_t ew[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) { cw[b] = R.rc[b]; ew[b] = R.re[b]; }
-    __syncthreads();
-    if (k0 + kTK < a.k) load_a(k0 + kTK);
-    if (k0 + 2 * kTK < a.k) load_step(R, k0 + 2 * kTK);
-    // per 16-value MFMA slice: dequantize 8 values of each B tile, then the MFMAs
+    // A fragments of slice st + 1 are read while the MFMAs of slice st run
+    const uint32_t at = lds_a + (uint32_t)((s % kStagesA) * kAStageBytes);
+    u32x4 af[2][NRT];
+    auto read_slice = [&](u32x4* dst, int st) __attribute__((always_inline)) {
+      const uint32_t aslot = at + (((a_g4 + (uint32_t)st) ^ a_sw) << 4);
+      if constexpr (NRT >= 1) asm volatile("ds_read_b128 %0, %1" : "=v"(dst[0]) : "v"(aslot));
+      if constexpr (NRT >= 2) asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(dst[1]) : "v"(aslot));
+      if constexpr (NRT >= 3) asm volatile("ds_read_b128 %0, %1 offset:8192" : "=v"(dst[2]) : "v"(aslot));
+      if constexpr (NRT >= 4) asm volatile("ds_read_b128 %0, %1 offset:12288" : "=v"(dst[3]) : "v"(aslot));
+      static_assert(32 * kTK * 2 == 4096, "fragment stride");
+    };
+    read_slice(af[0], 0);
+    wait_lds<NRT, kNB>(cw);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      bf16x8 bf[NB];
+      bf16x8 bf[kNB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
+      for (int b = 0; b < kNB; ++b) {
         const uint32_t e = (ew[b] >> (8 * (st / 2))) & 0xffu;
         u32x4 d;
         if (fast) d = dequant8_fast(cw[b][st], e);
         else d = dequant8_any(cw[b][st], e);
         bf[b] = __builtin_bit_cast(bf16x8, d);
       }
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[buf][rt * 32 + lc][32 * g + 8 * st]);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[rt][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[b], acc[rt][b], 0, 0, 0);
+      u32x4* cur = af[st & 1];
+      if (st < 3) {
+        read_slice(af[(st + 1) & 1], st + 1);
+        wait_lds<NRT, NRT>(cur);
+      } else {
+        wait_lds<0, NRT>(cur);
       }
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int b = 0; b < kNB; ++b)
+          acc[rt][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur[rt]), bf[b], acc[rt][b], 0, 0, 0);
     }
   };
 
-  // two register sets, two LDS buffers: step s uses set s % 2 and buffer s % 2. Writing
-  // buffer s % 2 at step s is safe: every wave finished reading it (step s - 2) before the
-  // barrier of step s - 1. K is a multiple of 2 kTK, so the loop body is the same for every
-  // iteration; one copy of the loop per count of row fragments.
+  // four steps (one exponent group) per iteration, then the two steps left when the step
+  // count is not a multiple of 4. One copy of the loop per count of row fragments.
   auto run = [&](auto NC) __attribute__((always_inline)) {
-    StepRegs r0, r1;
-    load_step(r0, 0);
-    load_a(0);
-    load_step(r1, kTK);
-    for (int k0 = 0; k0 < a.k; k0 += 2 * kTK) {
-      consume(r0, 0, k0, NC);
-      consume(r1, 1, k0 + kTK, NC);
+    // the first loads in the order the steps issue theirs: exponent group 0, (activations 0,
+    // weight block 0), activations 1
+    load_e(ecur, 0);
+    mem_order();
+    load_a(0, 0);
+    mem_order();
+    load_b(0, 0);
+    mem_order();
+    load_a(1, min(1, nsteps - 1));
+    mem_order();
+    int s = 0;
+    for (; s + 4 <= nsteps; s += 4) {
+      step(s, std::integral_constant<int, 0>{}, NC);
+      step(s + 1, std::integral_constant<int, 1>{}, NC);
+      step(s + 2, std::integral_constant<int, 2>{}, NC);
+      step(s + 3, std::integral_constant<int, 3>{}, NC);
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) ecur[b] = enext[b];
+    }
+    if (s < nsteps) {
+      step(s, std::integral_constant<int, 0>{}, NC);
+      step(s + 1, std::integral_constant<int, 1>{}, NC);
     }
   };
   switch (nrt) {
@@ -292,7 +410,8 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
     default: run(std::integral_constant<int, 4>{}); break;
   }
 
-  // epilogue: element i of a 32x32 tile sits at row (i/4)*8 + g*4 + i%4, column lc
+  // epilogue: element i of a 32x32 tile sits at row (i/4)*8 + g*4 + i%4, column lc. h goes
+  // out in the permuted pair order of each 8 columns (the down projection reads it as is).
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
@@ -301,15 +420,100 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
       if (t.row0 + r >= t.n) continue;
       const int64_t pos = t.p0 + t.row0 + r;
       if constexpr (NMAT == 2) {
+        const int col = wcol(lc);
+        if (col >= a.rows_per_expert) continue;
         const float gv = acc[rt][0][i], uv = acc[rt][1][i];
         const float hv = gv / (1.0f + __expf(-gv)) * uv;
-        static_cast<uint16_t*>(a.c)[pos * a.ldc + t.col0 + wave * 32 + lc] = (uint16_t)f32_to_bf16_rne(hv);
+        const int j = col & 7;
+        const int pcol = (col & ~7) | ((j & 1) ? 4 + (j >> 1) : (j >> 1));
+        static_cast<uint16_t*>(a.c)[pos * a.ldc + pcol] = (uint16_t)f32_to_bf16_rne(hv);
       } else {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          static_cast<float*>(a.c)[pos * a.ldc + t.col0 + wave * 64 + b * 32 + lc] = acc[rt][b][i];
+        for (int b = 0; b < kNB; ++b) {
+          const int col = wcol(b * 32 + lc);
+          if (col < a.rows_per_expert) static_cast<float*>(a.c)[pos * a.ldc + col] = acc[rt][b][i];
+        }
       }
     }
+}
+
+// Row-tile classes of a group of n > 0 rows: x = tiles with 4 row fragments (the full ones,
+// and a last one of more than 96 rows), y / z / w = 1 if the last tile has 3 / 2 / 1.
+__device__ __forceinline__ int4 tile_classes(int n) {
+  const int full = n / kTM, rem = n % kTM;
+  const int c = (rem > 0 && rem <= 96) ? (rem + 31) / 32 : 0;
+  return make_int4(full + (rem > 96 ? 1 : 0), c == 3, c == 2, c == 1);
+}
+
+struct PermArgs {
+  const uint16_t* x;          // bf16 [m][hidden]
+  int64_t n8;                 // m * hidden / 8
+  uint16_t* xp;
+  const int32_t* offsets;     // dispatch results
+  const int32_t* active;
+  const int32_t* n_active;
+  int m, with_shared;
+  int32_t* items;             // out: row tiles, heaviest first
+};
+
+// The last workgroup (256 threads) writes the sorted row-tile list: every tile with 4 row
+// fragments, then the last tiles with 3, 2 and 1, groups in order within each class. The
+// other workgroups permute x -> xp: every 8 values in the pair order (x0,x2)(x4,x6)(x1,x3)
+// (x5,x7) of the weight unpack (the gate/up activations, copied as they are into LDS by the
+// grouped GEMM).
+__global__ __launch_bounds__(256) void permute_rows_kernel(PermArgs p) {
+  if (blockIdx.x + 1 < gridDim.x) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < p.n8) *reinterpret_cast<uint4*>(p.xp + i * 8) = permute8(*reinterpret_cast<const uint4*>(p.x + i * 8));
+    return;
+  }
+  __shared__ int4 wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int na = *p.n_active, ng = na + p.with_shared;
+  auto rows_of = [&](int g) { return g < na ? p.offsets[p.active[g] + 1] - p.offsets[p.active[g]] : p.m; };
+  // exclusive block scan of v (tot: the block's sum)
+  auto scan = [&](int4 v, int4& tot) {
+    int4 inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int a0 = __shfl_up(inc.x, o), a1 = __shfl_up(inc.y, o), a2 = __shfl_up(inc.z, o), a3 = __shfl_up(inc.w, o);
+      if (lane >= o) { inc.x += a0; inc.y += a1; inc.z += a2; inc.w += a3; }
+    }
+    if (lane == 63) wtot[w] = inc;
+    __syncthreads();
+    int4 base = make_int4(0, 0, 0, 0);
+    tot = make_int4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int4 t = wtot[i];
+      if (i < w) { base.x += t.x; base.y += t.y; base.z += t.z; base.w += t.w; }
+      tot.x += t.x; tot.y += t.y; tot.z += t.z; tot.w += t.w;
+    }
+    __syncthreads();
+    return make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
+  };
+  int4 T = make_int4(0, 0, 0, 0);
+  for (int g0 = 0; g0 < ng; g0 += 256) {
+    const int g = g0 + tid;
+    int4 tot;
+    scan(g < ng ? tile_classes(rows_of(g)) : make_int4(0, 0, 0, 0), tot);
+    T.x += tot.x; T.y += tot.y; T.z += tot.z; T.w += tot.w;
+  }
+  int4 run = make_int4(0, T.x, T.x + T.y, T.x + T.y + T.z);   // where each class starts
+  for (int g0 = 0; g0 < ng; g0 += 256) {
+    const int g = g0 + tid;
+    const int n = g < ng ? rows_of(g) : 0;
+    const int4 v = g < ng ? tile_classes(n) : make_int4(0, 0, 0, 0);
+    int4 tot;
+    const int4 ex = scan(v, tot);
+    if (g < ng) {
+      for (int mt = 0; mt < v.x; ++mt) p.items[run.x + ex.x + mt] = g << 16 | mt;
+      const int last = g << 16 | (n / kTM);
+      if (v.y) p.items[run.y + ex.y] = last;
+      if (v.z) p.items[run.z + ex.z] = last;
+      if (v.w) p.items[run.w + ex.w] = last;
+    }
+    run.x += tot.x; run.y += tot.y; run.z += tot.z; run.w += tot.w;
+  }
 }
 
 // y[t] = sum_j w[t][j] * o[inv[t*K+j]] + g[t] * o[m*K + t]
@@ -338,8 +542,8 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(const float* o, const i
   *reinterpret_cast<f32x4*>(y + (int64_t)t * hidden + n4 * 4) = acc;
 }
 
-constexpr int kTNGate = 128;     // columns per matrix in the gate/up tiles
-constexpr int kTNDown = 256;     // columns in the down tiles
+constexpr int kTNGate = kWaves * kWaveCols / 2;   // columns per matrix in the gate/up tiles
+constexpr int kTNDown = kWaves * kWaveCols;       // columns in the down tiles
 
 int grid_for(int m, int top_k, int n_exp, int shared, int nct) {
   // upper bound of row tiles: every group may waste one partial tile
@@ -351,28 +555,48 @@ int grid_for(int m, int top_k, int n_exp, int shared, int nct) {
 
 }  // namespace
 
-size_t prefill_workspace_extra_bytes(int, int n_exp, int) { return (size_t)(n_exp + 2) * 4; }
+// extra region: the dispatch kernel's tile starts [n_exp + 2], the sorted row tiles (at most
+// one partial tile per group beyond the full ones), then the permuted activations; each part
+// 256-byte aligned
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+static size_t items_offset(int n_exp) { return round256((size_t)(n_exp + 2) * 4); }
+static size_t max_items(int m, int n_exp, int top_k) { return (size_t)(m * top_k + m) / kTM + n_exp + 1; }
+static size_t xp_offset(int m, int n_exp, int top_k) { return items_offset(n_exp) + round256(max_items(m, n_exp, top_k) * 4); }
 
 hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s) {
   const bfp_moe_layer* L = p.L;
   const int shared = L->sh_gate.fmt != 0;
   const int H = (int)L->hidden, F = (int)L->inter, K = L->top_k;
-  if (F % kTNGate != 0 || H % kTNDown != 0 || H % kTK != 0 || F % kTK != 0) return hipErrorNotSupported;
-  const int32_t* tile_start = p.tile_start;
+  // K steps come in weight blocks of two; the last column tile may be partial
+  if (H % (kTK * kBBlk) != 0 || F % (kTK * kBBlk) != 0 || F % 8 != 0) return hipErrorNotSupported;
+  // activations and one expert's weights are addressed with 32-bit byte offsets
+  if ((int64_t)F * H / 2 >= (1ll << 31)) return hipErrorNotSupported;
+  if ((int64_t)p.m * H * 2 >= (1ll << 31) || ((int64_t)p.m * K + p.m) * F * 2 >= (1ll << 31)) return hipErrorNotSupported;
+  const int32_t* tile_start = p.extra;
+  char* extra = reinterpret_cast<char*>(p.extra);
+  int32_t* items = reinterpret_cast<int32_t*>(extra + items_offset(L->n_experts));
+  uint16_t* xp = reinterpret_cast<uint16_t*>(extra + xp_offset(p.m, L->n_experts, K));
+  PermArgs pa{};
+  pa.x = p.x; pa.n8 = (int64_t)p.m * H / 8; pa.xp = xp;
+  pa.offsets = p.offsets; pa.active = p.active; pa.n_active = p.n_active;
+  pa.m = p.m; pa.with_shared = shared; pa.items = items;
+  hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((pa.n8 + 255) / 256 + 1)), dim3(256), 0, s, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   PfArgs a{};
   a.active = p.active; a.n_active = p.n_active; a.offsets = p.offsets; a.perm = p.perm;
-  a.tile_start = tile_start; a.with_shared = shared; a.m = p.m; a.top_k = K;
+  a.tile_start = tile_start; a.items = items; a.with_shared = shared; a.m = p.m; a.top_k = K;
   // gate/up + SwiGLU -> h (bf16)
   a.exp0 = L->gate.exp; a.code0 = L->gate.code; a.exp1 = L->up.exp; a.code1 = L->up.code;
   if (shared) {
     a.sexp0 = L->sh_gate.exp; a.scode0 = L->sh_gate.code; a.sexp1 = L->sh_up.exp; a.scode1 = L->sh_up.code;
   }
   a.rows_per_expert = F; a.k = H;
-  a.a = p.x; a.lda = H; a.a_by_token = 1;
+  a.a = xp; a.lda = H; a.a_by_token = 1; a.a_bytes = (uint32_t)((int64_t)p.m * H * 2);
   a.c = p.h; a.ldc = F;
-  hipLaunchKernelGGL((grouped_gemm_kernel<2>), dim3(grid_for(p.m, K, L->n_experts, shared, F / kTNGate)),
+  hipLaunchKernelGGL((grouped_gemm_kernel<2>), dim3(grid_for(p.m, K, L->n_experts, shared, (F + kTNGate - 1) / kTNGate)),
                      dim3(kPT), 0, s, a);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   // down -> o (fp32)
   PfArgs b = a;
@@ -380,9 +604,9 @@ hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s) {
   b.sexp0 = shared ? L->sh_down.exp : nullptr; b.scode0 = shared ? L->sh_down.code : nullptr;
   b.sexp1 = nullptr; b.scode1 = nullptr;
   b.rows_per_expert = H; b.k = F;
-  b.a = p.h; b.lda = F; b.a_by_token = 0;
+  b.a = p.h; b.lda = F; b.a_by_token = 0; b.a_bytes = (uint32_t)(((int64_t)p.m * K + shared * p.m) * F * 2);
   b.c = p.o; b.ldc = H;
-  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(grid_for(p.m, K, L->n_experts, shared, H / kTNDown)),
+  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(grid_for(p.m, K, L->n_experts, shared, (H + kTNDown - 1) / kTNDown)),
                      dim3(kPT), 0, s, b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 grid((H / 4 + 255) / 256, p.m);
@@ -391,5 +615,9 @@ hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s) {
 }
 
 int prefill_tile_rows() { return kTM; }
+
+size_t prefill_workspace_extra_bytes(int m, int n_exp, int top_k, int hidden) {
+  return xp_offset(m, n_exp, top_k) + (size_t)m * hidden * sizeof(uint16_t);
+}
 
 }  // namespace bfp
