@@ -58,7 +58,13 @@ struct MoeGemvArgs {
   void* y;                                          // [pairs][ldy], row = pair position
   int64_t ldy;
   int y_bf16;
+  const int32_t* tile_start;                        // non-null: the groups cut into row tiles of
+  int tile_m;                                       // tile_m pairs (dispatch's list), one per
+                                                    // workgroup row; null: one group per row
 };
+// Row-tile height of the decode expert kernels when m > 1 (a kernel built for more rows per
+// group holds more registers, and almost every group has one or two pairs).
+constexpr int kDecodeTileRows = 2;
 hipError_t moe_gemv_launch(const MoeGemvArgs& a, int nmat, hipStream_t s);
 
 struct CombineArgs {

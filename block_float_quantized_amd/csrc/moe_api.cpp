@@ -81,6 +81,7 @@ Layout layout(const bfp_moe_layer* L, int64_t m, bool with_experts) {
     }
     y.h = place(off, (size_t)pairs * F * 4);
     y.o = place(off, (size_t)pairs * H * 4);
+    y.extra = place(off, (size_t)(E + 2) * 4);      // row-tile starts of the groups
   }
   y.total = off;
   return y;
@@ -172,6 +173,10 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
     d.tile_m = bfp::prefill_tile_rows();
     d.with_shared = shared;
     d.tile_start = at<int32_t>(ws, ly.extra);
+  } else if (m > 1) {
+    d.tile_m = bfp::kDecodeTileRows;
+    d.with_shared = shared;
+    d.tile_start = at<int32_t>(ws, ly.extra);
   }
   if ((e = bfp::dispatch_launch(d, s)) != hipSuccess) return BFP_E_DEVICE;
 
@@ -197,6 +202,7 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
   gu.m = (int)m; gu.top_k = L->top_k;
   gu.x = x; gu.ldx = L->hidden; gu.x_by_token = 1; gu.x_bf16 = 1;
   gu.y = h; gu.ldy = L->inter; gu.y_bf16 = 0;
+  gu.tile_start = d.tile_start; gu.tile_m = d.tile_m;
   if ((e = bfp::moe_gemv_launch(gu, 2, s)) != hipSuccess) return BFP_E_DEVICE;
 
   bfp::MoeGemvArgs dn = gu;

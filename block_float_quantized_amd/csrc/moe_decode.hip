@@ -37,8 +37,19 @@ template <int NMAT, bool XB, int MBMAX, int LPR>
 __global__ __launch_bounds__(kMoeThreads) void moe_gemv_kernel(MoeGemvArgs ma, int kc) {
   extern __shared__ uint32_t xs[];
   __shared__ int xrow[32], yrow[32];
-  const int d = blockIdx.y;
   const int na = *ma.n_active;
+  int d = blockIdx.y, r0 = 0;     // group, and its first pair in this workgroup's tile
+  if (ma.tile_start) {
+    const int ng = na + (ma.scode0 != nullptr ? 1 : 0);
+    if ((int)blockIdx.y >= ma.tile_start[ng]) return;
+    int lo = 0, hi = ng - 1;      // last group whose first tile is <= blockIdx.y
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (ma.tile_start[mid] <= (int)blockIdx.y) lo = mid; else hi = mid - 1;
+    }
+    d = lo;
+    r0 = ((int)blockIdx.y - ma.tile_start[lo]) * ma.tile_m;
+  }
   const bool shared = d == na && ma.scode0 != nullptr;
   if (d > na || (d == na && !shared)) return;
   int e = -1, p0, n;
@@ -50,9 +61,12 @@ __global__ __launch_bounds__(kMoeThreads) void moe_gemv_kernel(MoeGemvArgs ma, i
     p0 = ma.m * ma.top_k;
     n = ma.m;
   }
+  p0 += r0;
+  n -= r0;
+  if (ma.tile_start && n > ma.tile_m) n = ma.tile_m;
   if ((int)threadIdx.x < n) {
     const int pos = p0 + threadIdx.x;
-    const int tok = shared ? (int)threadIdx.x : ma.perm[pos] / ma.top_k;
+    const int tok = shared ? pos - ma.m * ma.top_k : ma.perm[pos] / ma.top_k;
     xrow[threadIdx.x] = ma.x_by_token ? tok : pos;
     yrow[threadIdx.x] = pos;
   }
@@ -88,7 +102,10 @@ hipError_t launch_lpr(const MoeGemvArgs& ma, hipStream_t s) {
   // enough row tiles for the smallest rows-per-workgroup a group can pick (RT = 1 when
   // more than 8 pairs share an expert); workgroups past the end of a group exit
   constexpr int RPW = (kMoeThreads / kWave) * (kWave / LPR);
-  const int groups = (ma.m * ma.top_k < 256 ? ma.m * ma.top_k : 256) + (ma.scode0 ? 1 : 0);
+  const int pairs = ma.m * ma.top_k;
+  int groups = (pairs < 256 ? pairs : 256) + (ma.scode0 ? 1 : 0);
+  if (ma.tile_start)   // at most one partial tile per group beyond pairs / tile_m full ones
+    groups += pairs / ma.tile_m + (ma.scode0 ? ma.m / ma.tile_m : 0);
   dim3 grid((ma.rows_per_expert + RPW - 1) / RPW, groups);
   hipLaunchKernelGGL((moe_gemv_kernel<NMAT, XB, MBMAX, LPR>), grid, dim3(kMoeThreads), lds, s, ma, kc);
   return hipGetLastError();
@@ -107,6 +124,10 @@ hipError_t launch_mbmax(const MoeGemvArgs& ma, hipStream_t s) {
 
 template <int NMAT, bool XB>
 hipError_t launch_x(const MoeGemvArgs& ma, hipStream_t s) {
+  if (ma.tile_start) {
+    if (ma.tile_m != kDecodeTileRows) return hipErrorInvalidValue;
+    return launch_mbmax<NMAT, XB, kDecodeTileRows>(ma, s);
+  }
   switch (mb_bucket(ma.m)) {
     case 1: return launch_mbmax<NMAT, XB, 1>(ma, s);
     case 2: return launch_mbmax<NMAT, XB, 2>(ma, s);
