@@ -98,6 +98,37 @@ def test_moe_decode_matches_oracle(moe_full, m):
     assert_within(y, ref, norm, TOL, what=f"moe decode m={m}")
 
 
+def test_moe_decode_crowded_experts(moe_full):
+    """Decode with every token routed to the same 8 experts (a large router bias on them):
+    each group holds all 32 pairs and is cut into many row tiles; the shared group too."""
+    layer, dev, bank = moe_full
+    note("moe decode m=32 crowded")
+    m = 32
+    bias = np.zeros(256, np.float32)
+    bias[[3, 17, 42, 64, 99, 128, 200, 255]] = 40.0 + np.arange(8, dtype=np.float32)
+    devb = bfq.MoeLayer(**{**dev.__dict__, "router_bias": dev_f32(bias)})
+    x = synth.moe_tokens(m, 5)
+    ids = torch.empty((m, 8), dtype=torch.int32, device="cuda")
+    y = bfq.bfp_moe_forward(devb, dev_bf16(x), topk_ids=ids).cpu().numpy()
+    rt = oracle.route(x, layer["router"], 8, bias=bias, sh_gate_bits=layer["sh_gate_w"])
+    assert np.array_equal(ids.cpu().numpy(), rt["ids"])
+    assert set(np.unique(rt["ids"])) == {3, 17, 42, 64, 99, 128, 200, 255}
+    ref, norm = oracle.moe_decode(bank, x, rt)
+    assert_within(y, ref, norm, TOL, what="moe decode crowded")
+
+
+@pytest.mark.parametrize("m", [2, 5])
+def test_moe_decode_small_odd_batches(moe_full, m):
+    """Row tiles of two pairs with a one-pair tail (odd m: the shared group)."""
+    layer, dev, bank = moe_full
+    note(f"moe decode m={m}")
+    x = synth.moe_tokens(m, 9)
+    y = bfq.bfp_moe_forward(dev, dev_bf16(x)).cpu().numpy()
+    rt = oracle.route(x, layer["router"], 8, sh_gate_bits=layer["sh_gate_w"])
+    ref, norm = oracle.moe_decode(bank, x, rt)
+    assert_within(y, ref, norm, TOL, what=f"moe decode m={m}")
+
+
 def test_moe_decode_deterministic_and_row_invariant(moe_full):
     layer, dev, bank = moe_full
     note("moe decode determinism")
