@@ -15,11 +15,12 @@
 //    them heaviest first (row fragments that hold rows), and workgroup j takes column tile
 //    j % nct of sorted row tile j / nct, so that the long tiles start first.
 //  * Every operand reaches LDS by buffer loads that write LDS directly (no registers, no
-//    waits in the issuing wave): activation rows per K step of 64 (three steps in flight),
+//    waits in the issuing wave): activation rows per K step of 64 (two steps in flight),
 //    weight codes per block of two steps with 4 lanes per column (every load instruction
-//    touches 16 lines and uses 64 bytes of each), the block exponents into registers. One
-//    barrier per step; the waits for the loads are counted by hand, since the compiler
-//    cannot see which LDS range a load fills.
+//    touches 16 lines and uses 64 bytes of each), the block exponents into registers. Each
+//    ring slot is a separate LDS array named at compile time (the loop is unrolled over a
+//    4-step cycle), so the compiler can tell the slot being read from those being filled;
+//    one barrier per step, after a counted wait for the step's own loads.
 //  * v_mfma_f32_32x32x16_bf16 with fp32 accumulation; each wave owns all 128 rows of the
 //    tile and 64 output columns.
 //    A and B share one permutation of K inside every 8-value group (the order the BFP4
@@ -47,7 +48,7 @@ constexpr int kPT = 256;         // threads per workgroup (two workgroups per CU
 constexpr int kWaves = kPT / 64;
 constexpr int kNB = 2;           // 32-column B tiles per wave
 constexpr int kWaveCols = 32 * kNB;
-constexpr int kStagesA = 3;      // activation steps in the LDS ring
+constexpr int kStagesA = 2;      // activation steps in the LDS ring
 constexpr int kAStageBytes = kTM * kTK * 2;
 constexpr int kBBlk = 2;         // K steps per weight-code block
 constexpr int kBRing = 2;        // weight-code blocks in the LDS ring
@@ -153,7 +154,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // and kNB = 2 B tiles of 32 columns: NMAT = 2 -> the same 32 columns of gate and of up (the
 // SwiGLU pair lands in one lane), NMAT = 1 -> 64 adjacent columns. A workgroup therefore
 // covers TN = 4 * 64 / NMAT columns of each matrix (two workgroups per CU: the LDS rings
-// below take 80 KB each).
+// below take 64 KB each).
 //
 // Every operand goes through LDS, loaded by buffer loads straight into LDS (no registers):
 //  * activations, per K step of 64: kTM rows of 128 bytes, gathered by row, in a ring of
@@ -165,16 +166,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Lane group g = lane / 32 takes K values [32g, 32g + 32) of a step, 8 per MFMA; its A
 // fragment reads the same K values. Both operand reads use XOR-swizzled 16-byte slots, so
 // the 8 lanes a read serves at once hit distinct banks.
-
-// Wait until at most N of this wave's LDS reads are outstanding, then redefine the NR
-// fragments (an empty statement that claims to write them), so that nothing reading them
-// can be scheduled before the wait.
-template <int N, int NR>
-__device__ __forceinline__ void wait_lds(u32x4* r) {
-  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
-#pragma unroll
-  for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(r[i]));
-}
 
 // A pointer every lane holds the same value of, moved to scalar registers.
 __device__ __forceinline__ void* uniform_ptr(const void* p) {
@@ -196,8 +187,17 @@ __device__ __forceinline__ void mem_order() { asm volatile("" ::: "memory"); }
 template <int NMAT>
 __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
   constexpr int TN = kWaves * kWaveCols / NMAT;   // columns per matrix per workgroup
-  __shared__ __align__(16) uint8_t As[kStagesA][kAStageBytes];
-  __shared__ __align__(16) uint8_t Bs[kBRing][kBBlockBytes];
+  // one array per ring slot: each gets its own alias scope, so the compiler can tell a read
+  // of one slot from the loads still filling another and waits only for the right ones
+  __shared__ __align__(16) uint8_t As0[kAStageBytes], As1[kAStageBytes];
+  __shared__ __align__(16) uint8_t Bs0[kBBlockBytes], Bs1[kBBlockBytes];
+  static_assert(kStagesA == 2 && kBRing == 2, "ring slots are named arrays");
+  auto a_slot = [&](auto I) -> uint8_t* {
+    if constexpr (decltype(I)::value % 2 == 0) return As0; else return As1;
+  };
+  auto b_slot = [&](auto I) -> uint8_t* {
+    if constexpr (decltype(I)::value % 2 == 0) return Bs0; else return Bs1;
+  };
   TileInfo t;
   if (!find_tile<TN>(a, t)) return;
 
@@ -243,10 +243,11 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
     const int chunk = (lane % 8) ^ (rr % 8);
     asrc[q] = (uint32_t)(((int64_t)arow(rr) * a.lda + chunk * 8) * 2);
   }
-  auto load_a = [&](int stage, int step) __attribute__((always_inline)) {
+  auto load_a = [&](auto STAGE, int step) __attribute__((always_inline)) {
+    uint8_t* dst = a_slot(STAGE) + kAQ * wave * 1024;
 #pragma unroll
     for (int q = 0; q < kAQ; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (__attribute__((address_space(3))) void*)&As[stage][(kAQ * wave + q) * 1024], 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (__attribute__((address_space(3))) void*)(dst + q * 1024), 16,
                                                asrc[q], step * kTK * 2, 0, 0);
   };
   // weight-code loads: 4 instructions per block, instruction q covering this wave's columns
@@ -260,12 +261,12 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
     const int j = (lane % 4) ^ ((lane / 8) % 4);
     bsrc[q] = (uint32_t)(wcol(c) * (a.k / 2) + 16 * j);
   }
-  auto load_b = [&](int slot, int blk) __attribute__((always_inline)) {
+  auto load_b = [&](auto SLOT, int blk) __attribute__((always_inline)) {
+    uint8_t* dst = b_slot(SLOT) + wave * kBWaveBytes;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 ? crs0 : crs1,
-                                               (__attribute__((address_space(3))) void*)&Bs[slot][wave * kBWaveBytes + q * 1024], 16,
-                                               bsrc[q], blk * kBColBytes, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 ? crs0 : crs1, (__attribute__((address_space(3))) void*)(dst + q * 1024),
+                                               16, bsrc[q], blk * kBColBytes, 0, 0);
   };
   // exponent loads: per B tile, the 16 bytes of this lane's column covering 4 steps
   uint32_t eoff[kNB];
@@ -276,13 +277,11 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
     for (int b = 0; b < kNB; ++b) E[b] = __builtin_amdgcn_raw_buffer_load_b128(b == 0 ? ers0 : ers1, eoff[b], grp * 16, 0);
   };
 
-  // LDS byte addresses: A row lc of stage 0 with its swizzle, and the code slots of this
-  // lane's two columns b * 32 + lc in wave block 0
-  const uint32_t lds_a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&As[0][0] + (uint32_t)(lc * kTK * 2);
-  const uint32_t a_g4 = (uint32_t)(4 * g), a_sw = (uint32_t)(lc % 8);
-  const uint32_t lds_b = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&Bs[0][0] +
-                         (uint32_t)(wave * kBWaveBytes + (lc / 2) * 128 + (lc % 2) * 64);
-  const uint32_t b_sw = (uint32_t)((lc / 2) % 4);
+  // operand reads, ordinary LDS loads. A: row rt * 32 + lc of the step's stage, chunk 4 g + st
+  // at slot (4 g + st) ^ (lc % 8). B: this lane's column b * 32 + lc, chunk j = 2 (step % 2) + g
+  // at byte (c / 2) 128 + ((c % 2) 4 + (j ^ (c / 2) % 4)) 16 of the wave's part of the block.
+  const int a_off = lc * kTK * 2, a_g4 = 4 * g, a_sw = lc % 8;
+  const int b_off = wave * kBWaveBytes + (lc / 2) * 128 + (lc % 2) * 64, b_sw = (lc / 2) % 4;
 
   // rows of this tile that exist (wave-uniform): MFMAs of fragments past them are skipped
   const int nrt = (min(kTM, t.n - t.row0) + 31) / 32;
@@ -296,27 +295,28 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
 #pragma unroll
     for (int b = 0; b < kNB; ++b) acc[rt][b] = f32x16{};
 
-  // Step s (SP = s % 4): wait until this wave's loads of step s have landed, one barrier
-  // (every wave's have; every wave is done with the slots refilled next), issue the
-  // activations of step s + 2, on even steps the weight block of steps s + 2 and s + 3, on
-  // SP = 0 the exponents of steps s + 4 .. s + 7, then compute. Loads past the end repeat
-  // the last step, block or group, so every step issues the same loads. Per wave a step
-  // issues 4 activation loads, 4 weight loads on even steps and 2 exponent loads on SP = 0,
-  // in that order; counting those issued after the ones step s needs (its activations,
-  // issued two steps earlier, and on even steps its weight block, issued right after them)
-  // gives the wait below.
+  // Step s (I = SP = s % 4 at compile time): wait until this wave's loads of step s have
+  // landed (and its LDS reads are done), one barrier (every wave's have; every wave is done
+  // with the slots refilled next), issue the activations of step s + 1, on even steps the
+  // weight block of steps s + 2 and s + 3, on SP = 0 the exponents of steps s + 4 .. s + 7, then
+  // compute. Loads past the end repeat the last step, block or group, so every step issues
+  // the same loads. Per wave a step issues 4 activation loads, 4 weight loads on even steps
+  // and 2 exponent loads on SP = 0, in that order; counting those issued after the ones step s
+  // needs (its activations, issued one step earlier, and on even steps its weight block,
+  // issued two steps earlier) gives the wait below.
   u32x4 ecur[kNB], enext[kNB];
-  auto step = [&](int s, auto SPC, auto NC) __attribute__((always_inline)) {
-    constexpr int SP = decltype(SPC)::value;
+  auto step = [&](int s, auto IC, auto NC) __attribute__((always_inline)) {
+    constexpr int I = decltype(IC)::value;
+    constexpr int SP = I % 4;
     constexpr int NRT = decltype(NC)::value;
-    wait_vm<SP == 0 ? 4 : SP == 1 ? 10 : SP == 2 ? 6 : 8>();
+    wait_vm<SP == 0 ? 0 : SP == 1 ? 6 : SP == 2 ? 0 : 4>();
     mem_order();
     __builtin_amdgcn_s_barrier();
     mem_order();
-    load_a((s + 2) % kStagesA, min(s + 2, nsteps - 1));
+    load_a(std::integral_constant<int, (I + 1) % 2>{}, min(s + 1, nsteps - 1));
     mem_order();
     if constexpr (SP % 2 == 0) {
-      load_b((s / 2 + 1) % kBRing, min(s / 2 + 1, nblk - 1));
+      load_b(std::integral_constant<int, (I / 2 + 1) % 2>{}, min(s / 2 + 1, nblk - 1));
       mem_order();
     }
     if constexpr (SP == 0) {
@@ -324,12 +324,10 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
       mem_order();
     }
     // this step's code chunks (16 bytes = 32 values per column) and exponents
-    const uint32_t bj = (uint32_t)(2 * (SP % 2) + g);
-    const uint32_t bb = lds_b + (uint32_t)(((s / 2) % kBRing) * kBBlockBytes) + ((bj ^ b_sw) << 4);
+    const uint8_t* bb = b_slot(std::integral_constant<int, I / 2>{}) + b_off + (((2 * (SP % 2) + g) ^ b_sw) << 4);
     u32x4 cw[kNB];
-    static_assert(kNB == 2 && 16 * 128 == 2048, "tile stride");
-    asm volatile("ds_read_b128 %0, %1" : "=v"(cw[0]) : "v"(bb));
-    asm volatile("ds_read_b128 %0, %1 offset:2048" : "=v"(cw[1]) : "v"(bb));
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) cw[b] = *reinterpret_cast<const u32x4*>(bb + b * 16 * 128);
     uint32_t ew[kNB];
 #pragma unroll
     for (int b = 0; b < kNB; ++b) ew[b] = (ecur[b][SP] >> (16 * g)) & 0xffffu;
@@ -337,69 +335,57 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
 #pragma unroll
     for (int b = 0; b < kNB; ++b) ok = ok && ((ew[b] & 0xffu) - 8u) <= 239u && ((ew[b] >> 8) - 8u) <= 239u;
     const bool fast = __builtin_amdgcn_ballot_w64(!ok) == 0;
-    // A fragments of slice st + 1 are read while the MFMAs of slice st run
-    const uint32_t at = lds_a + (uint32_t)((s % kStagesA) * kAStageBytes);
-    u32x4 af[2][NRT];
-    auto read_slice = [&](u32x4* dst, int st) __attribute__((always_inline)) {
-      const uint32_t aslot = at + (((a_g4 + (uint32_t)st) ^ a_sw) << 4);
-      if constexpr (NRT >= 1) asm volatile("ds_read_b128 %0, %1" : "=v"(dst[0]) : "v"(aslot));
-      if constexpr (NRT >= 2) asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(dst[1]) : "v"(aslot));
-      if constexpr (NRT >= 3) asm volatile("ds_read_b128 %0, %1 offset:8192" : "=v"(dst[2]) : "v"(aslot));
-      if constexpr (NRT >= 4) asm volatile("ds_read_b128 %0, %1 offset:12288" : "=v"(dst[3]) : "v"(aslot));
-      static_assert(32 * kTK * 2 == 4096, "fragment stride");
-    };
-    read_slice(af[0], 0);
-    wait_lds<NRT, kNB>(cw);
+    // the step's weights dequantized first (one fast/slow decision per slice pair), then the
+    // MFMAs and their LDS reads as one straight-line stretch the scheduler can interleave
+    bf16x8 bf[4][kNB];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      bf16x8 bf[kNB];
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int b = 0; b < kNB; ++b) {
         const uint32_t e = (ew[b] >> (8 * (st / 2))) & 0xffu;
         u32x4 d;
         if (fast) d = dequant8_fast(cw[b][st], e);
         else d = dequant8_any(cw[b][st], e);
-        bf[b] = __builtin_bit_cast(bf16x8, d);
+        bf[st][b] = __builtin_bit_cast(bf16x8, d);
       }
-      u32x4* cur = af[st & 1];
-      if (st < 3) {
-        read_slice(af[(st + 1) & 1], st + 1);
-        wait_lds<NRT, NRT>(cur);
-      } else {
-        wait_lds<0, NRT>(cur);
+    const uint8_t* at = a_slot(IC) + a_off;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const uint8_t* as = at + (((a_g4 + st) ^ a_sw) << 4);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(as + rt * 32 * kTK * 2);
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) acc[rt][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[st][b], acc[rt][b], 0, 0, 0);
       }
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int b = 0; b < kNB; ++b)
-          acc[rt][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cur[rt]), bf[b], acc[rt][b], 0, 0, 0);
     }
-  };
-
-  // four steps (one exponent group) per iteration, then the two steps left when the step
-  // count is not a multiple of 4. One copy of the loop per count of row fragments.
-  auto run = [&](auto NC) __attribute__((always_inline)) {
-    // the first loads in the order the steps issue theirs: exponent group 0, (activations 0,
-    // weight block 0), activations 1
-    load_e(ecur, 0);
-    mem_order();
-    load_a(0, 0);
-    mem_order();
-    load_b(0, 0);
-    mem_order();
-    load_a(1, min(1, nsteps - 1));
-    mem_order();
-    int s = 0;
-    for (; s + 4 <= nsteps; s += 4) {
-      step(s, std::integral_constant<int, 0>{}, NC);
-      step(s + 1, std::integral_constant<int, 1>{}, NC);
-      step(s + 2, std::integral_constant<int, 2>{}, NC);
-      step(s + 3, std::integral_constant<int, 3>{}, NC);
+    if constexpr (SP == 3) {
 #pragma unroll
       for (int b = 0; b < kNB; ++b) ecur[b] = enext[b];
     }
-    if (s < nsteps) {
-      step(s, std::integral_constant<int, 0>{}, NC);
+  };
+
+  // four steps per iteration (the ring slots of every step known at compile time), then the
+  // two steps left when the step count is not a multiple of 4. One copy of the loop per count
+  // of row fragments.
+  auto run = [&](auto NC) __attribute__((always_inline)) {
+    // the first loads in the order the steps issue theirs: exponent group 0, weight block 0,
+    // activations 0
+    load_e(ecur, 0);
+    mem_order();
+    load_b(std::integral_constant<int, 0>{}, 0);
+    mem_order();
+    load_a(std::integral_constant<int, 0>{}, 0);
+    mem_order();
+    int s = 0;
+    for (; s + 4 <= nsteps; s += 4) {
+      step(s + 0, std::integral_constant<int, 0>{}, NC);
+      step(s + 1, std::integral_constant<int, 1>{}, NC);
+      step(s + 2, std::integral_constant<int, 2>{}, NC);
+      step(s + 3, std::integral_constant<int, 3>{}, NC);
+    }
+    if (s < nsteps) {   // nsteps is even
+      step(s + 0, std::integral_constant<int, 0>{}, NC);
       step(s + 1, std::integral_constant<int, 1>{}, NC);
     }
   };
