@@ -26,12 +26,13 @@ signed zero, subnormals, the byte layout, where activations are rounded), the or
 takes one stated reading; each function says which.
 
 Modules: ``bfp`` (encode/decode/storage sizes), ``linalg`` (bf16 rounding, GEMM,
-SwiGLU, error normaliser), ``moe`` (router, top-k, decode and prefill MoE, dispatch).
+SwiGLU, greedy pick, error normaliser), ``moe`` (router, top-k, decode and prefill MoE, dispatch).
 Every function here is pinned by ``tests/test_oracle_*.py`` against hand-worked values,
 brute force, exact rational arithmetic, invariants or byte counts printed on the pages.
 """
 from . import bfp, linalg, moe  # noqa: F401
 from .bfp import (BFP4, BFP8, NonFiniteError, code_bytes, decode, encode, exp_bytes,  # noqa: F401
                   mantissa_bits, storage_bytes, unpack_codes)
-from .linalg import (bf16_round, bf16_to_f64, gemm, normaliser, rel_err, silu, swiglu)  # noqa: F401
+from .linalg import (bf16_round, bf16_to_f64, gemm, greedy_pick, normaliser, rel_err, silu,  # noqa: F401
+                     swiglu)
 from .moe import dispatch, moe_decode, moe_prefill, route  # noqa: F401

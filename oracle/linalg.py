@@ -11,6 +11,11 @@ and every weight is read once per step).
 
 SwiGLU. h = silu(g) * u with silu(g) = g / (1 + exp(-g)), in fp64.
 
+Greedy pick. The token greedy decoding emits is the column of the largest LM-head logit
+("Qwen3.6-35B-A3B ...", section "Fused decode kernels": greedy argmax over the tiled
+logits, up to 16 rows). The pages say nothing of ties or NaN; the reading taken: the
+first such column, NaN counting as larger than every number, -0 equal to +0.
+
 Error metric. A GPU result y is compared per output element with
 |y - y_oracle| / sum_k |x_k * w_k|, the normaliser computed here in fp64 from the same
 operands; if the normaliser is 0 the values must be equal.
@@ -100,3 +105,24 @@ def rel_err(y: np.ndarray, y_ref: np.ndarray, norm: np.ndarray) -> np.ndarray:
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(norm > 0, d / np.where(norm > 0, norm, 1.0), np.where(d == 0, 0.0, math.inf))
     return r
+
+
+def greedy_pick(y: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per row of logits y [M][N]: (index, value) of the first column holding the row's
+    maximum, NaN counting as larger than any number (so the first NaN wins) and -0 as equal
+    to +0. A plain scan over the columns in order; returns int64 [M] and y's dtype [M]."""
+    y = np.asarray(y)
+    m, n = y.shape
+    idx = np.zeros(m, dtype=np.int64)
+    val = np.zeros(m, dtype=y.dtype)
+    for i in range(m):
+        best = 0
+        for j in range(1, n):
+            if math.isnan(y[i, best]):
+                break
+            v = y[i, j]
+            if math.isnan(v) or v > y[i, best]:
+                best = j
+        idx[i] = best
+        val[i] = y[i, best]
+    return idx, val

@@ -119,3 +119,42 @@ def test_silu_and_swiglu():
 def test_rel_err_zero_normaliser():
     r = oracle.rel_err(np.array([0.0, 1.0, 2.0]), np.array([0.0, 0.5, 2.0]), np.array([0.0, 0.0, 4.0]))
     assert r[0] == 0.0 and math.isinf(r[1]) and r[2] == 0.0
+
+
+def test_greedy_pick_hand_cases():
+    nan, inf = math.nan, math.inf
+    rows = [
+        ([1.0, 3.0, 3.0, 2.0], 1),        # tie: first column
+        ([1.0, nan, 5.0, nan], 1),        # NaN above every number, first NaN
+        ([-inf, -inf, -inf], 0),          # all equal
+        ([-0.0, 0.0], 0),                 # -0 equals +0
+        ([-1.0, 0.0, -0.0], 1),
+        ([-2.0, -1.0, -1.5], 1),          # all negative
+        ([7.0], 0),                       # one column
+        ([0.0, inf, 1e308, inf], 1),
+    ]
+    for vals, want in rows:
+        idx, val = oracle.greedy_pick(np.array([vals]))
+        assert idx[0] == want, (vals, idx[0])
+        assert (math.isnan(val[0]) and math.isnan(vals[want])) or val[0] == vals[want]
+    # rows are independent, dtype kept
+    idx, val = oracle.greedy_pick(np.array([[0.0, 2.0], [5.0, 1.0]], dtype=np.float32))
+    assert idx.tolist() == [1, 0] and val.dtype == np.float32
+
+
+def test_greedy_pick_vs_brute_force_and_numpy():
+    # small integer values: many ties; NaNs sprinkled in some rows
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        n = int(rng.integers(1, 12))
+        y = rng.integers(-2, 3, size=(3, n)).astype(np.float64)
+        if trial % 4 == 0:
+            y[rng.integers(0, 3), rng.integers(0, n)] = math.nan
+        idx, val = oracle.greedy_pick(y)
+        for i in range(3):
+            # definition by sorting: order columns by (NaN first, value descending, index ascending)
+            order = sorted(range(n), key=lambda j: (0 if math.isnan(y[i, j]) else 1,
+                                                    0.0 if math.isnan(y[i, j]) else -y[i, j], j))
+            assert idx[i] == order[0]
+            # numpy's argmax follows the same rule (first maximum, first NaN)
+            assert idx[i] == int(np.argmax(y[i]))
