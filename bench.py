@@ -64,7 +64,7 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_bfp4_gateup_m1_hbm_traffic.md")
 HEADLINE_SOURCES = ("block_float_quantized_amd/csrc/gemv_impl.hpp", "block_float_quantized_amd/csrc/gemv_b4_bf16x.hip",
                     "block_float_quantized_amd/csrc/bfp_device.hpp", "block_float_quantized_amd/csrc/gemv.hip")
-HEADLINE_KERNEL = "gemv_kernel<4, 1, 1, 16, 2, 2, 2, true, 256>"
+HEADLINE_KERNEL = "gemv_kernel<4, 1, 1, 16, 2, 2, 2, true, 256, false>"
 COPY_BYTES = 512 << 20
 
 
@@ -270,8 +270,9 @@ def cpu_baseline(c: dict, rows: int, xbits: np.ndarray) -> dict:
 
 # ---- other workloads -----------------------------------------------------------------------
 
-def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32"):
-    """Time bfp_gemm on one matrix over cold replicas for each x in xs_bits (dict M -> bits)."""
+def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32", argmax_name=None):
+    """Time bfp_gemm on one matrix over cold replicas for each x in xs_bits (dict M -> bits);
+    with argmax_name, also bfp_gemm_argmax (greedy pick per row, no outputs written)."""
     import torch
     import block_float_quantized_amd as bfq
     base = quantize(fmt, w)
@@ -288,6 +289,18 @@ def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32"):
                                 "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                                 "bytes": nbytes, "replicas": R, "tok_per_s": round(m / (ms * 1e-3), 1)}
         log(f"{name} M={m}: {ms * 1e3:.2f} us")
+        if argmax_name:
+            idx = torch.empty((m,), dtype=torch.int32, device="cuda")
+            val = torch.empty((m,), dtype=torch.float32, device="cuda")
+            ws = workspace(bfq.bfp_gemm_argmax_workspace_bytes(base, m))
+            ms = timed(lambda i: bfq.bfp_gemm_argmax(mats[i % R], x, idx=idx, val=val, workspace=ws),
+                       args.steps, args.warmup)
+            nbytes = base.nbytes + m * base.k * 2 + m * 8
+            out[f"{argmax_name} M={m}"] = {"us_per_call": round(ms * 1e3, 2),
+                                           "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                           "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                                           "bytes": nbytes, "replicas": R, "tok_per_s": round(m / (ms * 1e-3), 1)}
+            log(f"{argmax_name} M={m}: {ms * 1e3:.2f} us")
     del mats
     torch.cuda.empty_cache()
     return out
@@ -398,7 +411,8 @@ def main():
         lm = synth.dense_weights(0, 3, "lm", 151936, 2048, 0.02)
         workloads.update(gemv_workload(args, "BFP8 LM head 2048->151936", lm,
                                        8, {1: synth.proj_case(1, 0, with_lm=False)["x"],
-                                           16: synth.proj_case(16, 0, with_lm=False)["x"]}))
+                                           16: synth.proj_case(16, 0, with_lm=False)["x"]},
+                                       argmax_name="BFP8 LM head + greedy argmax 2048->151936"))
         del lm
         workloads.update(moe_workloads(args))
     line = {

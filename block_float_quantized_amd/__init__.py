@@ -6,7 +6,7 @@ provides device memory and streams. There is no CPU fallback: if ``libbfp.so`` i
 fails to load, every call raises.
 
 Functions keep the C names (``bfp_quantize``, ``bfp_dequantize``, ``bfp_gemm``,
-``bfp_moe_route``, ``bfp_moe_dispatch``, ``bfp_moe_workspace_bytes``, ``bfp_moe_forward``)
+``bfp_gemm_argmax``, ``bfp_moe_route``, ``bfp_moe_dispatch``, ``bfp_moe_workspace_bytes``, ``bfp_moe_forward``)
 and take torch tensors where the C call takes device pointers.
 """
 from __future__ import annotations
@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "BFP4", "BFP8", "BfpError", "BfpMatrix", "MoeLayer", "lib", "library_path",
-    "bfp_quantize", "bfp_dequantize", "bfp_gemm", "bfp_gemm_workspace_bytes", "bfp_moe_route", "bfp_moe_dispatch",
+    "bfp_quantize", "bfp_dequantize", "bfp_gemm", "bfp_gemm_workspace_bytes", "bfp_gemm_argmax",
+    "bfp_gemm_argmax_workspace_bytes", "bfp_moe_route", "bfp_moe_dispatch",
     "bfp_moe_workspace_bytes", "bfp_moe_forward", "exp_bytes", "code_bytes",
 ]
 
@@ -75,6 +76,10 @@ _SIGS = {
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]),
+    "bfp_gemm_argmax_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Tensor), ctypes.c_int64]),
+    "bfp_gemm_argmax": (ctypes.c_int32, [ctypes.POINTER(_Tensor), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]),
     "bfp_moe_route_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_MoeLayer), ctypes.c_int64]),
     "bfp_moe_route": (ctypes.c_int32, [ctypes.POINTER(_MoeLayer), ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -217,6 +222,34 @@ def bfp_gemm(w: BfpMatrix, x: torch.Tensor, w_up: BfpMatrix | None = None, out_d
                         _ptr(workspace), workspace.numel(), _stream(stream))
     _check("bfp_gemm", st)
     return out
+
+
+def bfp_gemm_argmax_workspace_bytes(w: BfpMatrix, m: int) -> int:
+    return int(lib().bfp_gemm_argmax_workspace_bytes(ctypes.byref(w.view()), m))
+
+
+def bfp_gemm_argmax(w: BfpMatrix, x: torch.Tensor, idx: torch.Tensor | None = None, val: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Per row of x ([m][k] bf16, m <= 32): (int32 column, fp32 value) of the largest entry of
+    x W^T, the first such column on ties, without materialising x W^T.
+
+    ``workspace`` (uint8 device tensor of at least bfp_gemm_argmax_workspace_bytes bytes) is
+    made here when not given.
+    """
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a row-major [m][k] device tensor")
+    m = x.shape[0]
+    if idx is None:
+        idx = torch.empty((m,), dtype=torch.int32, device=x.device)
+    if val is None:
+        val = torch.empty((m,), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        need = bfp_gemm_argmax_workspace_bytes(w, m)
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    st = lib().bfp_gemm_argmax(ctypes.byref(w.view()), _ptr(x), _dt(x), m, x.stride(0), _ptr(idx), _ptr(val),
+                               _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("bfp_gemm_argmax", st)
+    return idx, val
 
 
 @dataclass

@@ -134,7 +134,7 @@ int32_t bfp_gemm(const bfp_tensor* w, const bfp_tensor* w_up, int32_t epilogue, 
   const size_t need = bfp::gemv_workspace_bytes(w->fmt, epilogue == BFP_EPI_SWIGLU, w->n, w->k, m);
   if (need > 0 && (!ws || ws_bytes < need)) return BFP_E_WORKSPACE;
   if (ws && !aligned16(ws)) return BFP_E_ALIGN;
-  bfp::GemvParams g;
+  bfp::GemvParams g{};
   g.fmt = w->fmt;
   g.w_exp = w->exp; g.w_code = w->code;
   g.u_exp = epilogue == BFP_EPI_SWIGLU ? w_up->exp : nullptr;
@@ -143,6 +143,35 @@ int32_t bfp_gemm(const bfp_tensor* w, const bfp_tensor* w_up, int32_t epilogue, 
   g.x = x; g.ldx = ldx; g.x_bf16 = x_dtype == BFP_DT_BF16;
   g.m = m; g.y = y; g.ldy = ldy; g.y_bf16 = y_dtype == BFP_DT_BF16;
   g.ws = ws;
+  return from_hip(bfp::gemv_launch(g, static_cast<hipStream_t>(stream)));
+}
+
+size_t bfp_gemm_argmax_workspace_bytes(const bfp_tensor* w, int64_t m) {
+  if (check_tensor(w) != BFP_OK || m < 1 || m > BFP_GEMM_MAX_M) return 0;
+  return bfp::gemv_argmax_workspace_bytes(w->fmt, w->n, w->k, m);
+}
+
+int32_t bfp_gemm_argmax(const bfp_tensor* w, const void* x, int32_t x_dtype, int64_t m, int64_t ldx,
+                        int32_t* idx, float* val, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_tensor(w);
+  if (st != BFP_OK) return st;
+  if (x_dtype != BFP_DT_F32 && x_dtype != BFP_DT_BF16) return BFP_E_ARG;
+  if (x_dtype != BFP_DT_BF16) return BFP_E_UNSUPPORTED;
+  if (!x || !idx || !val || !ws) return BFP_E_ARG;
+  if (m < 1 || m > BFP_GEMM_MAX_M) return BFP_E_SHAPE;
+  if (ldx < w->k) return BFP_E_SHAPE;
+  if (!aligned16(x) || ((ldx * 2) % 16) != 0) return BFP_E_ALIGN;
+  if (!aligned16(ws)) return BFP_E_ALIGN;
+  if (ws_bytes < bfp::gemv_argmax_workspace_bytes(w->fmt, w->n, w->k, m)) return BFP_E_WORKSPACE;
+  bfp::GemvParams g{};
+  g.fmt = w->fmt;
+  g.w_exp = w->exp; g.w_code = w->code;
+  g.n = w->n; g.k = w->k;
+  g.x = x; g.ldx = ldx; g.x_bf16 = 1;
+  g.m = m;
+  g.ws = ws;
+  g.am_idx = idx;
+  g.am_val = val;
   return from_hip(bfp::gemv_launch(g, static_cast<hipStream_t>(stream)));
 }
 

@@ -30,11 +30,21 @@ struct GemvParams {
   void* y;
   int64_t ldy;
   int y_bf16;
-  void* ws;                    // workspace of gemv_workspace_bytes bytes (or null when that is 0)
+  void* ws;                    // workspace of gemv_workspace_bytes bytes (or null when that is 0),
+                               // gemv_argmax_workspace_bytes in argmax mode
+  int32_t* am_idx;             // argmax mode (one matrix, bf16 x): per row of x, the column of the
+  float* am_val;               // largest output and its value; y is not written. Else null.
 };
 
 // Workspace bytes gemv_launch needs for these shapes (0: none).
 size_t gemv_workspace_bytes(int fmt, bool swiglu, int64_t n, int64_t k, int64_t m);
+
+// Workspace bytes of argmax mode.
+size_t gemv_argmax_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
+
+// The vector kernel's workgroups own at least this many weight rows each (bounds the argmax
+// candidates per row of x).
+constexpr int kVectorMinRowsPerWg = 8;
 
 hipError_t gemv_launch(const GemvParams& g, hipStream_t s);
 

@@ -41,7 +41,7 @@ hipError_t vector_launch(const GemvParams& g, hipStream_t s) {
 }
 
 hipError_t mfma_launch(const GemvParams& g, hipStream_t s) {
-  mg::MgArgs a;
+  mg::MgArgs a{};
   a.exp[0] = g.w_exp; a.code[0] = g.w_code;
   a.exp[1] = g.u_exp; a.code[1] = g.u_code;
   a.x = g.x; a.ldx = g.ldx;
@@ -51,6 +51,11 @@ hipError_t mfma_launch(const GemvParams& g, hipStream_t s) {
   a.ws = static_cast<float*>(g.ws);
   a.ks = 1; a.sps = 0; a.kc = 0; a.exp_vec = 0;
   a.code16 = (g.k % 32) == 0;
+  if (g.am_idx != nullptr) {
+    a.cand = static_cast<uint64_t*>(g.ws);
+    a.am_idx = g.am_idx;
+    a.am_val = g.am_val;
+  }
   return g.fmt == 4 ? mfma_gemv_launch_b4(a, g.x_bf16 != 0, s) : mfma_gemv_launch_b8(a, g.x_bf16 != 0, s);
 }
 
@@ -61,6 +66,12 @@ size_t gemv_workspace_bytes(int fmt, bool swiglu, int64_t n, int64_t k, int64_t 
   const int N = (int)n, K = (int)k, M = (int)m;
   if (fmt == 4) return swiglu ? mg::workspace_bytes<4, 2>(N, K, M) : mg::workspace_bytes<4, 1>(N, K, M);
   return swiglu ? mg::workspace_bytes<8, 2>(N, K, M) : mg::workspace_bytes<8, 1>(N, K, M);
+}
+
+size_t gemv_argmax_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m) {
+  if (use_vector(m)) return (size_t)m * ((n + kVectorMinRowsPerWg - 1) / kVectorMinRowsPerWg) * sizeof(uint64_t);
+  const int N = (int)n, K = (int)k, M = (int)m;
+  return fmt == 4 ? mg::argmax_workspace_bytes<4>(N, K, M) : mg::argmax_workspace_bytes<8>(N, K, M);
 }
 
 hipError_t gemv_launch(const GemvParams& g, hipStream_t s) {

@@ -4,7 +4,7 @@
 namespace bfp {
 
 hipError_t gemv_launch_b8_f32x(const GemvParams& g, hipStream_t s) {
-  gemv_detail::GemvArgs a;
+  gemv_detail::GemvArgs a{};
   a.exp0 = g.w_exp; a.code0 = g.w_code;
   a.exp1 = g.u_exp; a.code1 = g.u_code;
   a.x = g.x; a.ldx = g.ldx; a.y = g.y; a.ldy = g.ldy;

@@ -23,6 +23,7 @@
 //    and v_permlane16_swap; one lane per value writes y (with the SwiGLU epilogue).
 //  * Each lane's share of K and the order of its sums depend on K only, so row i of an
 //    M-row call is bit-identical to the same row computed alone.
+#include "argmax.hpp"
 #include "bfp_device.hpp"
 #include "bfp_internal.hpp"
 
@@ -42,6 +43,9 @@ struct GemvArgs {
   int n, k, m;
   int y_bf16;
   int kc;                                  // K values staged per LDS chunk
+  uint64_t* cand;                          // argmax mode: candidate keys [m][workgroups], else null
+  int32_t* am_idx;                         // argmax mode: per activation row, the column
+  float* am_val;                           //   and its value
 };
 
 // A unit: what one lane loads per row with one instruction.
@@ -261,8 +265,10 @@ __device__ __forceinline__ void compute_group(float (&acc)[NMAT][RT][MB], const 
 //
 // gemv_tile computes the rows [row_base, row_base + rows per workgroup) of one matrix view for
 // a.m activation rows; xrow/yrow (in LDS, or null for the identity) map activation slot i to
-// the row of x it reads and the row of y it writes.
-template <int FMT, int MB, int RT, int LPR, int NMAT, int U, int BPU, bool XB, int kThreads>
+// the row of x it reads and the row of y it writes. With AM (argmax mode, one matrix) nothing is
+// written to y: the workgroup stores, per activation row, the key of its largest output
+// (argmax.hpp) in a.cand[i][blockIdx.x].
+template <int FMT, int MB, int RT, int LPR, int NMAT, int U, int BPU, bool XB, int kThreads, bool AM = false>
 __device__ __forceinline__ void gemv_tile(const GemvArgs& a, int row_base, const int* xrow, const int* yrow,
                                           uint32_t* xs) {
   using UT = Unit<FMT, BPU>;
@@ -333,6 +339,28 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& a, int row_base, const
 #pragma unroll
       for (int t = 0; t < NMAT; ++t) v[(r * MB + i) * NMAT + t] = acc[t][r][i];
   Red::run(v, lane);
+  if constexpr (AM) {
+    static_assert(NMAT == 1, "argmax of one matrix");
+    constexpr int RPW = (kThreads / kWave) * G * RT;    // weight rows per workgroup
+    __shared__ uint64_t keys[MB][RPW];
+    if (Red::writer(p)) {
+      const int first = Red::first_index(p);
+#pragma unroll
+      for (int q = 0; q < Red::kCount; ++q) {
+        const int r = (first + q) / MB, i = (first + q) % MB;
+        const int row = row0 + r;
+        keys[i][row - row_base] = (row < a.n && i < a.m) ? am::key_of(v[q], row) : am::kNone;
+      }
+    }
+    __syncthreads();
+    for (int i = wave; i < MB; i += kThreads / kWave) {
+      uint64_t k = am::kNone;
+      for (int j = lane; j < RPW; j += kWave) k = am::kmax(k, keys[i][j]);
+      k = am::lane_max<kWave>(k);
+      if (lane == 0 && i < a.m) a.cand[(int64_t)i * gridDim.x + blockIdx.x] = k;
+    }
+    return;
+  }
   if (!Red::writer(p)) return;
   const int first = Red::first_index(p);
 #pragma unroll
@@ -354,11 +382,11 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs& a, int row_base, const
   }
 }
 
-template <int FMT, int MB, int RT, int LPR, int NMAT, int U, int BPU, bool XB, int kThreads>
+template <int FMT, int MB, int RT, int LPR, int NMAT, int U, int BPU, bool XB, int kThreads, bool AM = false>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   extern __shared__ uint32_t xs[];
   constexpr int rows_per_wg = (kThreads / kWave) * (kWave / LPR) * RT;
-  gemv_tile<FMT, MB, RT, LPR, NMAT, U, BPU, XB, kThreads>(a, blockIdx.x * rows_per_wg, nullptr, nullptr, xs);
+  gemv_tile<FMT, MB, RT, LPR, NMAT, U, BPU, XB, kThreads, AM>(a, blockIdx.x * rows_per_wg, nullptr, nullptr, xs);
 }
 
 // ---- launch selection (host) --------------------------------------------------------------
@@ -387,7 +415,16 @@ hipError_t launch_th(const GemvArgs& a, size_t lds, hipStream_t s) {
   constexpr int RT = 1;
   constexpr int U = MB <= 4 ? 2 : 1;
   constexpr int rows_per_wg = (T / kWave) * (kWave / LPR) * RT;
+  static_assert(rows_per_wg >= kVectorMinRowsPerWg, "argmax workspace bound");
   const int grid = (a.n + rows_per_wg - 1) / rows_per_wg;
+  if constexpr (NMAT == 1 && XB) {
+    if (a.cand != nullptr) {
+      hipLaunchKernelGGL((gemv_kernel<FMT, MB, RT, LPR, NMAT, U, BPU, XB, T, true>), dim3(grid), dim3(T), lds, s, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return am::launch_rows<false>(a.cand, nullptr, 0, grid, a.m, a.am_idx, a.am_val, s);
+    }
+  }
   hipLaunchKernelGGL((gemv_kernel<FMT, MB, RT, LPR, NMAT, U, BPU, XB, T>), dim3(grid), dim3(T), lds, s, a);
   return hipGetLastError();
 }

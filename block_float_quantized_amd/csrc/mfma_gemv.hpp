@@ -30,6 +30,7 @@
 //    fp32 partial tile to the workspace and a second kernel adds the slices in slice order and
 //    applies the epilogue. The slicing and every summation order depend on N and K only, so
 //    row i of an m-row call is bit-identical to the same row computed alone.
+#include "argmax.hpp"
 #include "bfp_device.hpp"
 #include "bfp_internal.hpp"
 
@@ -57,6 +58,9 @@ struct MgArgs {
   int kc;            // K values staged per chunk (a whole number of steps)
   int exp_vec;       // a lane's exponent bytes may be read with one aligned load
   int code16;        // BFP4 rows start on 16-byte boundaries (K a multiple of 32)
+  uint64_t* cand;    // argmax mode: workspace (argmax_workspace_bytes), else null
+  int32_t* am_idx;   // argmax mode: per activation row, the column of the largest output
+  float* am_val;     //   and its value
 };
 
 // One step of one matrix as loaded by a wave: 16 weight rows x SK values, read row-contiguously
@@ -309,8 +313,10 @@ struct WaveLds {
 
 // FMT: 4 or 8. NMAT: 1, or 2 for SwiGLU (same columns of gate and up). MT: 16-row activation
 // tiles (1 for m <= 16, 2 for m <= 32). XS: bf16 planes per activation (1 bf16, 2 fp32).
-// G: 128-value units per step.
-template <int FMT, int NMAT, int MT, int XS, int G>
+// G: 128-value units per step. AM (argmax mode, one matrix, one slice): nothing is written to
+// y; the workgroup stores, per activation row, the key of its largest output (argmax.hpp) in
+// a.cand[i][blockIdx.x].
+template <int FMT, int NMAT, int MT, int XS, int G, bool AM = false>
 __global__ __launch_bounds__(kWaves * 64) void mfma_gemv_kernel(MgArgs a) {
   using R = StepRegs<FMT, G>;
   using W = WaveLds<FMT, G>;
@@ -438,6 +444,28 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_gemv_kernel(MgArgs a) {
     if (a.y_bf16) static_cast<uint16_t*>(a.y)[yo] = (uint16_t)f32_to_bf16_rne(out);
     else static_cast<float*>(a.y)[yo] = out;
   };
+  if constexpr (AM) {
+    static_assert(NMAT == 1, "argmax of one matrix");
+    // over the 16 columns of each wave (lanes with equal g), then over the four waves
+    __shared__ uint64_t keys[kWaves][MT * 16];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int yc = col0 + c;
+        uint64_t k = yc < a.n ? am::key_of(acc[0][mt][i], yc) : am::kNone;
+        k = am::lane_max<16>(k);
+        if (c == 0) keys[wave][mt * 16 + 4 * g + i] = k;
+      }
+    __syncthreads();
+    if (wave == 0 && lane < MT * 16 && lane < a.m) {
+      uint64_t k = keys[0][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) k = am::kmax(k, keys[w][lane]);
+      a.cand[(int64_t)lane * gridDim.x + blockIdx.x] = k;
+    }
+    return;
+  }
   if (a.ks == 1) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -511,6 +539,17 @@ size_t workspace_bytes(int n, int k, int m) {
   return ks > 1 ? (size_t)ks * NMAT * m * n * sizeof(float) : 0;
 }
 
+// Argmax mode's workspace: with one slice, the candidate keys [m][workgroups]; with several,
+// the fp32 outputs [m][n] (256-byte aligned size) and after them the slice partials.
+inline size_t am_outputs_bytes(int n, int m) { return ((size_t)m * n * sizeof(float) + 255) / 256 * 256; }
+template <int FMT>
+size_t argmax_workspace_bytes(int n, int k, int m) {
+  int ks, sps;
+  pick_slices(n, k, 128 * kG<FMT, 1>, ks, sps);
+  if (ks == 1) return (size_t)m * ((n + kCols - 1) / kCols) * sizeof(uint64_t);
+  return am_outputs_bytes(n, m) + workspace_bytes<FMT, 1>(n, k, m);
+}
+
 template <int FMT, int NMAT, int MT, int XS>
 hipError_t launch_mt(MgArgs a, hipStream_t s) {
   constexpr int G = kG<FMT, NMAT>;
@@ -528,12 +567,33 @@ hipError_t launch_mt(MgArgs a, hipStream_t s) {
   a.kc = steps * SK < slice_k ? steps * SK : slice_k;
   const size_t lds = stage_bytes(a.m, XS, a.kc) + (size_t)kWaves * NMAT * WaveLds<FMT, G>::kBytes;
   const dim3 grid((a.n + kCols - 1) / kCols, a.ks);
+  const bool am_mode = a.cand != nullptr;
+  if constexpr (NMAT == 1 && XS == 1) {
+    if (am_mode && a.ks == 1) {
+      hipLaunchKernelGGL((mfma_gemv_kernel<FMT, NMAT, MT, XS, G, true>), grid, dim3(kWaves * 64), lds, s, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return am::launch_rows<false>(a.cand, nullptr, 0, (int)grid.x, a.m, a.am_idx, a.am_val, s);
+    }
+    if (am_mode) {
+      // K is sliced: the fp32 outputs go to the workspace, then a per-row argmax over them
+      a.y = a.cand;
+      a.ldy = a.n;
+      a.y_bf16 = 0;
+      a.ws = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.cand) + am_outputs_bytes(a.n, a.m));
+    }
+  } else {
+    if (am_mode) return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL((mfma_gemv_kernel<FMT, NMAT, MT, XS, G>), grid, dim3(kWaves * 64), lds, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.ks == 1) return e;
-  const int64_t mn = (int64_t)a.m * a.n;
-  hipLaunchKernelGGL((slice_sum_kernel<NMAT>), dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (e == hipSuccess && a.ks > 1) {
+    const int64_t mn = (int64_t)a.m * a.n;
+    hipLaunchKernelGGL((slice_sum_kernel<NMAT>), dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s, a);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess || !am_mode) return e;
+  return am::launch_rows<true>(nullptr, static_cast<const float*>(a.y), a.n, a.n, a.m, a.am_idx, a.am_val, s);
 }
 
 template <int FMT, int XS>

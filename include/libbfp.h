@@ -134,6 +134,29 @@ int32_t bfp_gemm(const bfp_tensor *w, const bfp_tensor *w_up, int32_t epilogue,
                  void *y, int32_t y_dtype, int64_t ldy, void *ws, size_t ws_bytes,
                  void *stream);
 
+/* Workspace bytes bfp_gemm_argmax needs for an m-row call on w (0 if w or m is invalid). */
+size_t bfp_gemm_argmax_workspace_bytes(const bfp_tensor *w, int64_t m);
+
+/*
+ * Greedy pick over the outputs of a skinny matmul ("Qwen3.6-35B-A3B ...", "Fused decode
+ * kernels": greedy argmax on the tiled LM-head logits, with no vocabulary-wide copy of
+ * them). With y[i][j] the fp32 result bfp_gemm(w, NULL, BFP_EPI_NONE, x, BFP_DT_BF16, m,
+ * ...) would write, for every row i < m:
+ *   idx[i] = the smallest j < w->n with y[i][j] maximal, NaN counting as larger than any
+ *            number (the first NaN wins) and -0 as equal to +0;
+ *   val[i] = y[i][idx[i]] (a -0 reported as +0, a NaN as the quiet NaN 0x7fc00000).
+ * y itself is never written: each workgroup of the matmul reduces its own columns to one
+ * candidate per row, and a second kernel reduces the candidates of each row. The outputs
+ * are bit for bit those of this rule applied to bfp_gemm's y for the same m. x: device bf16
+ * [m][ldx] (BFP_DT_F32 gives BFP_E_UNSUPPORTED); m in 1..BFP_GEMM_MAX_M; idx: device
+ * int32 [m]; val: device fp32 [m]; ws: device workspace of at least
+ * bfp_gemm_argmax_workspace_bytes(w, m) bytes (BFP_E_WORKSPACE if smaller), 16-byte
+ * aligned, contents on entry and on return unspecified.
+ */
+int32_t bfp_gemm_argmax(const bfp_tensor *w, const void *x, int32_t x_dtype, int64_t m,
+                        int64_t ldx, int32_t *idx, float *val, void *ws, size_t ws_bytes,
+                        void *stream);
+
 /*
  * One MoE layer with BFP4 experts ("qwen3.6-a3b-blackhole", introduction; "Qwen3.6-35B-A3B
  * ...", "Precision as served" and "Fused decode kernels").
