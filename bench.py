@@ -216,7 +216,7 @@ def make_mlp(replicas: int, seed: int = 0):
     return c, mats
 
 
-def run_mlp(args, m, mats, xb):
+def run_mlp(args, m, mats, xb, batch_invariant=False):
     import torch
     import block_float_quantized_amd as bfq
     x = bf16_dev(xb)
@@ -229,12 +229,12 @@ def run_mlp(args, m, mats, xb):
 
     def step(i):
         g, u, d = mats[i % R]
-        bfq.bfp_gemm(g, x, w_up=u, out=h, workspace=ws_gu)
-        bfq.bfp_gemm(d, h, out_dtype=torch.bfloat16, out=y, workspace=ws_d)
+        bfq.bfp_gemm(g, x, w_up=u, out=h, workspace=ws_gu, batch_invariant=batch_invariant)
+        bfq.bfp_gemm(d, h, out_dtype=torch.bfloat16, out=y, workspace=ws_d, batch_invariant=batch_invariant)
 
     def gateup(i):
         g, u, _ = mats[i % R]
-        bfq.bfp_gemm(g, x, w_up=u, out=h, workspace=ws_gu)
+        bfq.bfp_gemm(g, x, w_up=u, out=h, workspace=ws_gu, batch_invariant=batch_invariant)
 
     ms_step = timed(step, args.steps, args.warmup)
     ms_gu = timed(gateup, args.steps, args.warmup)
@@ -398,6 +398,10 @@ def main():
             r = run_mlp(args, m, mats, synth.mlp_case(m, 0)["x"])
             workloads[f"dense BFP4 MLP M={m}"] = {k: round(v, 2) for k, v in r.items()}
             log(f"MLP M={m}: {r['us_per_call']:.2f} us")
+        # one summation order for every M (the matrix-core kernel at M = 1 as well)
+        r = run_mlp(args, 1, mats, synth.mlp_case(1, 0)["x"], batch_invariant=True)
+        workloads["dense BFP4 MLP M=1 batch-invariant"] = {k: round(v, 2) for k, v in r.items()}
+        log(f"MLP M=1 batch-invariant: {r['us_per_call']:.2f} us")
     cpu = None if args.no_cpu_baseline else cpu_baseline(c, args.cpu_rows, xb)
     del mats, c
     torch.cuda.empty_cache()

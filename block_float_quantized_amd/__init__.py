@@ -30,6 +30,7 @@ DT_F32 = 0
 DT_BF16 = 1
 EPI_NONE = 0
 EPI_SWIGLU = 1
+BATCH_INVARIANT = 0x100
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -78,8 +79,8 @@ _SIGS = {
                                   ctypes.c_size_t, ctypes.c_void_p]),
     "bfp_gemm_argmax_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Tensor), ctypes.c_int64]),
     "bfp_gemm_argmax": (ctypes.c_int32, [ctypes.POINTER(_Tensor), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
-                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                         ctypes.c_size_t, ctypes.c_void_p]),
+                                         ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "bfp_moe_route_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_MoeLayer), ctypes.c_int64]),
     "bfp_moe_route": (ctypes.c_int32, [ctypes.POINTER(_MoeLayer), ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -200,11 +201,12 @@ def bfp_gemm_workspace_bytes(w: BfpMatrix, m: int, w_up: BfpMatrix | None = None
 
 
 def bfp_gemm(w: BfpMatrix, x: torch.Tensor, w_up: BfpMatrix | None = None, out_dtype=torch.float32,
-             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+             batch_invariant: bool = False) -> torch.Tensor:
     """y = x W^T (or silu(x W^T) * (x Wup^T) when w_up is given); x is [m][k], m <= 32.
 
     ``workspace`` (uint8 device tensor of at least bfp_gemm_workspace_bytes bytes) is made
-    here when not given.
+    here when not given. ``batch_invariant``: row i is the same bits for every m.
     """
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a row-major [m][k] device tensor")
@@ -217,7 +219,7 @@ def bfp_gemm(w: BfpMatrix, x: torch.Tensor, w_up: BfpMatrix | None = None, out_d
         need = bfp_gemm_workspace_bytes(w, m, w_up)
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
     st = lib().bfp_gemm(ctypes.byref(vw), ctypes.byref(vu) if vu is not None else None,
-                        EPI_SWIGLU if w_up is not None else EPI_NONE,
+                        (EPI_SWIGLU if w_up is not None else EPI_NONE) | (BATCH_INVARIANT if batch_invariant else 0),
                         _ptr(x), _dt(x), m, x.stride(0), _ptr(out), _dt(out), out.stride(0),
                         _ptr(workspace), workspace.numel(), _stream(stream))
     _check("bfp_gemm", st)
@@ -229,9 +231,11 @@ def bfp_gemm_argmax_workspace_bytes(w: BfpMatrix, m: int) -> int:
 
 
 def bfp_gemm_argmax(w: BfpMatrix, x: torch.Tensor, idx: torch.Tensor | None = None, val: torch.Tensor | None = None,
-                    workspace: torch.Tensor | None = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+                    workspace: torch.Tensor | None = None, stream=None,
+                    batch_invariant: bool = False) -> tuple[torch.Tensor, torch.Tensor]:
     """Per row of x ([m][k] bf16, m <= 32): (int32 column, fp32 value) of the largest entry of
-    x W^T, the first such column on ties, without materialising x W^T.
+    x W^T, the first such column on ties, without materialising x W^T. ``batch_invariant`` as
+    in bfp_gemm.
 
     ``workspace`` (uint8 device tensor of at least bfp_gemm_argmax_workspace_bytes bytes) is
     made here when not given.
@@ -246,7 +250,8 @@ def bfp_gemm_argmax(w: BfpMatrix, x: torch.Tensor, idx: torch.Tensor | None = No
     if workspace is None:
         need = bfp_gemm_argmax_workspace_bytes(w, m)
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
-    st = lib().bfp_gemm_argmax(ctypes.byref(w.view()), _ptr(x), _dt(x), m, x.stride(0), _ptr(idx), _ptr(val),
+    st = lib().bfp_gemm_argmax(ctypes.byref(w.view()), _ptr(x), _dt(x), m, x.stride(0),
+                               BATCH_INVARIANT if batch_invariant else 0, _ptr(idx), _ptr(val),
                                _ptr(workspace), workspace.numel(), _stream(stream))
     _check("bfp_gemm_argmax", st)
     return idx, val

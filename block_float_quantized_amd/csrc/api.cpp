@@ -4,6 +4,7 @@
 // device work was queued. No C++ exception crosses this boundary.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <unordered_map>
 
@@ -106,7 +107,9 @@ int32_t bfp_dequantize(const bfp_tensor* w, int32_t out_dtype, void* out, void* 
 
 size_t bfp_gemm_workspace_bytes(const bfp_tensor* w, const bfp_tensor* w_up, int64_t m) {
   if (check_tensor(w) != BFP_OK || m < 1 || m > BFP_GEMM_MAX_M) return 0;
-  return bfp::gemv_workspace_bytes(w->fmt, w_up != nullptr, w->n, w->k, m);
+  // enough for both kernel choices (with and without BFP_GEMM_BATCH_INVARIANT)
+  return std::max(bfp::gemv_workspace_bytes(w->fmt, w_up != nullptr, w->n, w->k, m, false),
+                  bfp::gemv_workspace_bytes(w->fmt, w_up != nullptr, w->n, w->k, m, true));
 }
 
 int32_t bfp_gemm(const bfp_tensor* w, const bfp_tensor* w_up, int32_t epilogue, const void* x,
@@ -114,6 +117,10 @@ int32_t bfp_gemm(const bfp_tensor* w, const bfp_tensor* w_up, int32_t epilogue, 
                  void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_tensor(w);
   if (st != BFP_OK) return st;
+  const int32_t flags = epilogue & ~0xff;
+  epilogue &= 0xff;
+  if ((flags & ~BFP_GEMM_BATCH_INVARIANT) != 0) return BFP_E_ARG;
+  const bool invariant = (flags & BFP_GEMM_BATCH_INVARIANT) != 0;
   if (epilogue == BFP_EPI_NONE) {
     if (w_up) return BFP_E_ARG;
   } else if (epilogue == BFP_EPI_SWIGLU) {
@@ -131,7 +138,7 @@ int32_t bfp_gemm(const bfp_tensor* w, const bfp_tensor* w_up, int32_t epilogue, 
   if (ldx < w->k || ldy < w->n) return BFP_E_SHAPE;
   const int64_t xs = x_dtype == BFP_DT_BF16 ? 2 : 4;
   if (!aligned16(x) || ((ldx * xs) % 16) != 0) return BFP_E_ALIGN;
-  const size_t need = bfp::gemv_workspace_bytes(w->fmt, epilogue == BFP_EPI_SWIGLU, w->n, w->k, m);
+  const size_t need = bfp::gemv_workspace_bytes(w->fmt, epilogue == BFP_EPI_SWIGLU, w->n, w->k, m, invariant);
   if (need > 0 && (!ws || ws_bytes < need)) return BFP_E_WORKSPACE;
   if (ws && !aligned16(ws)) return BFP_E_ALIGN;
   bfp::GemvParams g{};
@@ -143,18 +150,22 @@ int32_t bfp_gemm(const bfp_tensor* w, const bfp_tensor* w_up, int32_t epilogue, 
   g.x = x; g.ldx = ldx; g.x_bf16 = x_dtype == BFP_DT_BF16;
   g.m = m; g.y = y; g.ldy = ldy; g.y_bf16 = y_dtype == BFP_DT_BF16;
   g.ws = ws;
+  g.invariant = invariant;
   return from_hip(bfp::gemv_launch(g, static_cast<hipStream_t>(stream)));
 }
 
 size_t bfp_gemm_argmax_workspace_bytes(const bfp_tensor* w, int64_t m) {
   if (check_tensor(w) != BFP_OK || m < 1 || m > BFP_GEMM_MAX_M) return 0;
-  return bfp::gemv_argmax_workspace_bytes(w->fmt, w->n, w->k, m);
+  return std::max(bfp::gemv_argmax_workspace_bytes(w->fmt, w->n, w->k, m, false),
+                  bfp::gemv_argmax_workspace_bytes(w->fmt, w->n, w->k, m, true));
 }
 
 int32_t bfp_gemm_argmax(const bfp_tensor* w, const void* x, int32_t x_dtype, int64_t m, int64_t ldx,
-                        int32_t* idx, float* val, void* ws, size_t ws_bytes, void* stream) {
+                        int32_t flags, int32_t* idx, float* val, void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_tensor(w);
   if (st != BFP_OK) return st;
+  if ((flags & ~BFP_GEMM_BATCH_INVARIANT) != 0) return BFP_E_ARG;
+  const bool invariant = (flags & BFP_GEMM_BATCH_INVARIANT) != 0;
   if (x_dtype != BFP_DT_F32 && x_dtype != BFP_DT_BF16) return BFP_E_ARG;
   if (x_dtype != BFP_DT_BF16) return BFP_E_UNSUPPORTED;
   if (!x || !idx || !val || !ws) return BFP_E_ARG;
@@ -162,7 +173,7 @@ int32_t bfp_gemm_argmax(const bfp_tensor* w, const void* x, int32_t x_dtype, int
   if (ldx < w->k) return BFP_E_SHAPE;
   if (!aligned16(x) || ((ldx * 2) % 16) != 0) return BFP_E_ALIGN;
   if (!aligned16(ws)) return BFP_E_ALIGN;
-  if (ws_bytes < bfp::gemv_argmax_workspace_bytes(w->fmt, w->n, w->k, m)) return BFP_E_WORKSPACE;
+  if (ws_bytes < bfp::gemv_argmax_workspace_bytes(w->fmt, w->n, w->k, m, invariant)) return BFP_E_WORKSPACE;
   bfp::GemvParams g{};
   g.fmt = w->fmt;
   g.w_exp = w->exp; g.w_code = w->code;
@@ -172,6 +183,7 @@ int32_t bfp_gemm_argmax(const bfp_tensor* w, const void* x, int32_t x_dtype, int
   g.ws = ws;
   g.am_idx = idx;
   g.am_val = val;
+  g.invariant = invariant;
   return from_hip(bfp::gemv_launch(g, static_cast<hipStream_t>(stream)));
 }
 

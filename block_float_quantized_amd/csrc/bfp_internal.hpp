@@ -34,13 +34,14 @@ struct GemvParams {
                                // gemv_argmax_workspace_bytes in argmax mode
   int32_t* am_idx;             // argmax mode (one matrix, bf16 x): per row of x, the column of the
   float* am_val;               // largest output and its value; y is not written. Else null.
+  int invariant;               // one summation order for every m (the matrix-core kernel at m = 1 too)
 };
 
 // Workspace bytes gemv_launch needs for these shapes (0: none).
-size_t gemv_workspace_bytes(int fmt, bool swiglu, int64_t n, int64_t k, int64_t m);
+size_t gemv_workspace_bytes(int fmt, bool swiglu, int64_t n, int64_t k, int64_t m, bool invariant);
 
 // Workspace bytes of argmax mode.
-size_t gemv_argmax_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
+size_t gemv_argmax_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m, bool invariant);
 
 // The vector kernel's workgroups own at least this many weight rows each (bounds the argmax
 // candidates per row of x).

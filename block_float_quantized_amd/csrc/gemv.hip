@@ -18,8 +18,9 @@ hipError_t mfma_gemv_launch_b8(const mg::MgArgs& a, bool x_bf16, hipStream_t s);
 namespace {
 
 // One activation row runs the vector-ALU kernel (it streams the weights faster when there is
-// a single row to multiply); 2..32 rows run the matrix-core kernel. BFP_GEMV_KERNEL=vector or
-// =mfma forces one kernel for every m (for measurement).
+// a single row to multiply); 2..32 rows run the matrix-core kernel. Batch-invariant calls run
+// the matrix-core kernel for every m, so that row i does not depend on m. BFP_GEMV_KERNEL=vector
+// or =mfma forces one kernel for every m in the other calls (for measurement).
 enum class Kernel { kAuto, kVector, kMfma };
 Kernel forced() {
   static const Kernel k = [] {
@@ -30,7 +31,8 @@ Kernel forced() {
   }();
   return k;
 }
-bool use_vector(int64_t m) {
+bool use_vector(int64_t m, bool invariant) {
+  if (invariant) return false;
   const Kernel k = forced();
   return k == Kernel::kVector || (k == Kernel::kAuto && m == 1);
 }
@@ -61,21 +63,21 @@ hipError_t mfma_launch(const GemvParams& g, hipStream_t s) {
 
 }  // namespace
 
-size_t gemv_workspace_bytes(int fmt, bool swiglu, int64_t n, int64_t k, int64_t m) {
-  if (use_vector(m)) return 0;
+size_t gemv_workspace_bytes(int fmt, bool swiglu, int64_t n, int64_t k, int64_t m, bool invariant) {
+  if (use_vector(m, invariant)) return 0;
   const int N = (int)n, K = (int)k, M = (int)m;
   if (fmt == 4) return swiglu ? mg::workspace_bytes<4, 2>(N, K, M) : mg::workspace_bytes<4, 1>(N, K, M);
   return swiglu ? mg::workspace_bytes<8, 2>(N, K, M) : mg::workspace_bytes<8, 1>(N, K, M);
 }
 
-size_t gemv_argmax_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m) {
-  if (use_vector(m)) return (size_t)m * ((n + kVectorMinRowsPerWg - 1) / kVectorMinRowsPerWg) * sizeof(uint64_t);
+size_t gemv_argmax_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m, bool invariant) {
+  if (use_vector(m, invariant)) return (size_t)m * ((n + kVectorMinRowsPerWg - 1) / kVectorMinRowsPerWg) * sizeof(uint64_t);
   const int N = (int)n, K = (int)k, M = (int)m;
   return fmt == 4 ? mg::argmax_workspace_bytes<4>(N, K, M) : mg::argmax_workspace_bytes<8>(N, K, M);
 }
 
 hipError_t gemv_launch(const GemvParams& g, hipStream_t s) {
-  if (use_vector(g.m)) return vector_launch(g, s);
+  if (use_vector(g.m, g.invariant != 0)) return vector_launch(g, s);
   return mfma_launch(g, s);
 }
 

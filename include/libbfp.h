@@ -64,6 +64,14 @@ typedef enum {
 enum { BFP_FMT_BFP4 = 4, BFP_FMT_BFP8 = 8 };
 enum { BFP_DT_F32 = 0, BFP_DT_BF16 = 1 };
 enum { BFP_EPI_NONE = 0, BFP_EPI_SWIGLU = 1 };
+/*
+ * Flag of bfp_gemm (or-ed into `epilogue`) and bfp_gemm_argmax: row i of the result is bit
+ * for bit the same for every m in 1..BFP_GEMM_MAX_M, whatever the other rows hold
+ * ("Qwen3.8-27B ...", "What changed in this release (s27v6-20261024)": each user's output in
+ * a batch equals its single-user output bit for bit). Costs speed at m = 1 (the matrix-core
+ * kernel runs where the vector kernel would be faster).
+ */
+#define BFP_GEMM_BATCH_INVARIANT 0x100
 
 /* Non-owning view of one BFP matrix in device memory (layout above). */
 typedef struct bfp_tensor {
@@ -108,8 +116,9 @@ int32_t bfp_quantize(int32_t fmt, const float *w, int64_t n, int64_t k,
 int32_t bfp_dequantize(const bfp_tensor *w, int32_t out_dtype, void *out, void *stream);
 
 /*
- * Workspace bytes bfp_gemm needs for an m-row call on w (with w_up for SWIGLU, else NULL);
- * 0 when it needs none. Depends on the shapes only (not on pointers or values).
+ * Workspace bytes bfp_gemm needs for an m-row call on w (with w_up for SWIGLU, else NULL),
+ * with or without BFP_GEMM_BATCH_INVARIANT; 0 when it needs none. Depends on the shapes only
+ * (not on pointers or values).
  */
 size_t bfp_gemm_workspace_bytes(const bfp_tensor *w, const bfp_tensor *w_up, int64_t m);
 
@@ -123,9 +132,10 @@ size_t bfp_gemm_workspace_bytes(const bfp_tensor *w, const bfp_tensor *w_up, int
  * weights are exact and sums are fp32. m = 1 runs on the vector ALUs (fp32 x exact as well);
  * m >= 2 runs on the bf16 matrix cores, where fp32 x enters as the sum of two bf16 values
  * (about 16 significant bits) and row i of the result does not depend on m or on the other
- * rows (same reduction order for every m in 2..32). w_up must be NULL for NONE and match w's
- * format and shape for
- * SWIGLU. ws: device workspace of at least bfp_gemm_workspace_bytes(w, w_up, m) bytes (may
+ * rows (same reduction order for every m in 2..32). With BFP_GEMM_BATCH_INVARIANT or-ed into
+ * `epilogue`, m = 1 runs on the matrix cores too, so that row i is the same for every m in
+ * 1..32; other bits of `epilogue` above the low byte give BFP_E_ARG. w_up must be NULL for
+ * NONE and match w's format and shape for SWIGLU. ws: device workspace of at least bfp_gemm_workspace_bytes(w, w_up, m) bytes (may
  * be NULL when that is 0; BFP_E_WORKSPACE if missing or smaller), 16-byte aligned, contents
  * on entry and on return unspecified. Calls sharing a workspace on different streams race.
  */
@@ -134,28 +144,30 @@ int32_t bfp_gemm(const bfp_tensor *w, const bfp_tensor *w_up, int32_t epilogue,
                  void *y, int32_t y_dtype, int64_t ldy, void *ws, size_t ws_bytes,
                  void *stream);
 
-/* Workspace bytes bfp_gemm_argmax needs for an m-row call on w (0 if w or m is invalid). */
+/* Workspace bytes bfp_gemm_argmax needs for an m-row call on w, with or without
+ * BFP_GEMM_BATCH_INVARIANT (0 if w or m is invalid). */
 size_t bfp_gemm_argmax_workspace_bytes(const bfp_tensor *w, int64_t m);
 
 /*
  * Greedy pick over the outputs of a skinny matmul ("Qwen3.6-35B-A3B ...", "Fused decode
  * kernels": greedy argmax on the tiled LM-head logits, with no vocabulary-wide copy of
- * them). With y[i][j] the fp32 result bfp_gemm(w, NULL, BFP_EPI_NONE, x, BFP_DT_BF16, m,
- * ...) would write, for every row i < m:
+ * them). With y[i][j] the fp32 result bfp_gemm(w, NULL, BFP_EPI_NONE | flags, x,
+ * BFP_DT_BF16, m, ...) would write, for every row i < m:
  *   idx[i] = the smallest j < w->n with y[i][j] maximal, NaN counting as larger than any
  *            number (the first NaN wins) and -0 as equal to +0;
  *   val[i] = y[i][idx[i]] (a -0 reported as +0, a NaN as the quiet NaN 0x7fc00000).
  * y itself is never written: each workgroup of the matmul reduces its own columns to one
  * candidate per row, and a second kernel reduces the candidates of each row. The outputs
- * are bit for bit those of this rule applied to bfp_gemm's y for the same m. x: device bf16
+ * are bit for bit those of this rule applied to bfp_gemm's y for the same m and flags.
+ * flags: 0 or BFP_GEMM_BATCH_INVARIANT (other bits give BFP_E_ARG). x: device bf16
  * [m][ldx] (BFP_DT_F32 gives BFP_E_UNSUPPORTED); m in 1..BFP_GEMM_MAX_M; idx: device
  * int32 [m]; val: device fp32 [m]; ws: device workspace of at least
  * bfp_gemm_argmax_workspace_bytes(w, m) bytes (BFP_E_WORKSPACE if smaller), 16-byte
  * aligned, contents on entry and on return unspecified.
  */
 int32_t bfp_gemm_argmax(const bfp_tensor *w, const void *x, int32_t x_dtype, int64_t m,
-                        int64_t ldx, int32_t *idx, float *val, void *ws, size_t ws_bytes,
-                        void *stream);
+                        int64_t ldx, int32_t flags, int32_t *idx, float *val, void *ws,
+                        size_t ws_bytes, void *stream);
 
 /*
  * One MoE layer with BFP4 experts ("qwen3.6-a3b-blackhole", introduction; "Qwen3.6-35B-A3B

@@ -84,16 +84,22 @@ def test_host_validation_before_any_launch():
     need = lib.bfp_gemm_argmax_workspace_bytes(ctypes.byref(lm), 1)
     assert need >= 151936 // 64 * 8
     assert lib.bfp_gemm_argmax_workspace_bytes(ctypes.byref(lm), 33) == 0
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 0, 2048, 16, 16, 16, need, None) == 2      # m = 0
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 33, 2048, 16, 16, 16, need, None) == 2     # m > 32
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 0, 1, 2048, 16, 16, 16, need, None) == 7      # fp32 x
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 2, 1, 2048, 16, 16, 16, need, None) == 1      # bad dtype
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2040, 16, 16, 16, need, None) == 2      # ldx < k
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 24, 1, 1, 2048, 16, 16, 16, need, None) == 3      # misaligned x
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2048, None, 16, 16, need, None) == 1    # no idx
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2048, 16, 16, None, need, None) == 1    # no workspace
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2048, 16, 16, 16, need - 1, None) == 5  # too small
-    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2048, 16, 16, 24, need, None) == 3      # misaligned ws
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 0, 2048, 0, 16, 16, 16, need, None) == 2      # m = 0
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 33, 2048, 0, 16, 16, 16, need, None) == 2     # m > 32
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 0, 1, 2048, 0, 16, 16, 16, need, None) == 7      # fp32 x
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 2, 1, 2048, 0, 16, 16, 16, need, None) == 1      # bad dtype
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2040, 0, 16, 16, 16, need, None) == 2      # ldx < k
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 24, 1, 1, 2048, 0, 16, 16, 16, need, None) == 3      # misaligned x
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2048, 0, None, 16, 16, need, None) == 1    # no idx
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2048, 0, 16, 16, None, need, None) == 1    # no workspace
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2048, 0, 16, 16, 16, need - 1, None) == 5  # too small
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2048, 0, 16, 16, 24, need, None) == 3      # misaligned ws
+    assert lib.bfp_gemm_argmax(ctypes.byref(lm), 16, 1, 1, 2048, 2, 16, 16, 16, need, None) == 1      # unknown flag
+    # batch-invariant flag: other high bits of the epilogue are rejected; the workspace query
+    # covers the matrix-core kernel at m = 1
+    assert lib.bfp_gemm(ctypes.byref(w), None, 0x200, 16, 1, 1, 64, 16, 0, 32, None, 0, None) == 1
+    assert lib.bfp_gemm(ctypes.byref(big), None, 0x100, 16, 1, 1, 16384, 16, 0, 64, None, 0, None) == 5
+    assert lib.bfp_gemm_workspace_bytes(ctypes.byref(big), None, 1) > 0
 
 
 def test_python_binding_refuses_without_library(monkeypatch, tmp_path):

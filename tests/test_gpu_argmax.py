@@ -140,6 +140,22 @@ def test_argmax_deterministic():
         assert torch.equal(i, a[0][0]) and torch.equal(v.view(torch.int32), a[0][1].view(torch.int32))
 
 
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+def test_argmax_batch_invariant_flag(fmt):
+    """With BFP_GEMM_BATCH_INVARIANT the pick and value of row i are the same for every m,
+    one-row calls included, and equal the first maximum of bfp_gemm's flagged outputs."""
+    note(f"argmax batch-invariant fmt={fmt}")
+    wm, wd, x64, xt = _case(fmt, 5000, 2048, 32, seed=40 + fmt)
+    i32, v32 = (t.cpu().numpy() for t in bfq.bfp_gemm_argmax(wm, xt, batch_invariant=True))
+    y = bfq.bfp_gemm(wm, xt, batch_invariant=True).cpu().numpy()
+    ref_idx, ref_val = _first_max(y)
+    assert np.array_equal(i32, ref_idx) and np.array_equal(_bits(v32), _bits(ref_val))
+    for a, b in [(0, 1), (9, 10), (31, 32), (4, 20)]:
+        i, v = (t.cpu().numpy() for t in bfq.bfp_gemm_argmax(wm, xt[a:b].contiguous(), batch_invariant=True))
+        assert np.array_equal(i, i32[a:b]) and np.array_equal(_bits(v), _bits(v32[a:b])), f"rows {a}:{b}"
+    _check_vs_oracle(i32, v32, oracle.gemm(x64, wd), oracle.normaliser(x64, wd), what="invariant")
+
+
 def _sampled(n, count, seed):
     return np.unique(np.concatenate([[0, n - 1], np.random.default_rng(seed).integers(0, n, count)]))
 

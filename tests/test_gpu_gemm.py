@@ -121,6 +121,34 @@ def test_gemm_rows_independent_of_m_long_k(x_dtype):
 
 
 @pytest.mark.parametrize("fmt", [BFP8, BFP4])
+@pytest.mark.parametrize("n,k,x_dtype,swiglu", [(300, 2064, "bf16", False), (96, 17408, "bf16", True),
+                                                 (200, 1040, "f32", False), (5000, 2048, "bf16", False)])
+def test_gemm_batch_invariant_flag(fmt, n, k, x_dtype, swiglu):
+    """With BFP_GEMM_BATCH_INVARIANT, row i of an m-row call is the same bits for every m in
+    1..32, the one-row call included (short and sliced K, SwiGLU, fp32 x, one and two row
+    tiles), and within the tolerance of the oracle."""
+    note(f"gemm batch-invariant flag fmt={fmt} n={n} k={k} x={x_dtype} swiglu={swiglu}")
+    wm, wd, x64, xt = _case(fmt, n, k, 32, seed=n + k + fmt, x_dtype=x_dtype)
+    um = ud = None
+    if swiglu:
+        wu = (np.random.default_rng(n).standard_normal((n, k)) * 0.02).astype(np.float32)
+        eu, cu = oracle.encode(wu, fmt)
+        ud = oracle.decode(eu, cu, fmt, n, k)
+        um = matrix_from_oracle(fmt, eu, cu, n, k)
+    y32 = bfq.bfp_gemm(wm, xt, w_up=um, batch_invariant=True).cpu().numpy()
+    for a, b in [(0, 1), (7, 8), (31, 32), (3, 5), (10, 26), (16, 32), (0, 17)]:
+        y = bfq.bfp_gemm(wm, xt[a:b].contiguous(), w_up=um, batch_invariant=True).cpu().numpy()
+        assert np.array_equal(y.view(np.uint32), y32[a:b].view(np.uint32)), f"rows {a}:{b} differ from the 32-row call"
+    if swiglu:
+        g, u = oracle.gemm(x64, wd), oracle.gemm(x64, ud)
+        ref = oracle.swiglu(g, u)
+        norm = 1.1 * oracle.normaliser(x64, wd) * np.abs(u) + np.abs(oracle.silu(g)) * oracle.normaliser(x64, ud)
+        assert_within(y32, ref, norm, TOL, extra=1e-6 * np.abs(ref), what="invariant swiglu")
+    else:
+        assert_within(y32, oracle.gemm(x64, wd), oracle.normaliser(x64, wd), TOL, what="invariant gemm")
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
 @pytest.mark.parametrize("wscale,xscale", [(2.0 ** -128, 2.0 ** 60), (2.0 ** -124, 2.0 ** 50),
                                            (2.0 ** 121, 2.0 ** -100)])
 def test_gemm_extreme_exponents(fmt, wscale, xscale):

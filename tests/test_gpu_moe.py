@@ -130,12 +130,21 @@ def test_moe_decode_small_odd_batches(moe_full, m):
 
 
 def test_moe_decode_deterministic_and_row_invariant(moe_full):
+    """Same input, same bits; and token t's output is the same bits whatever the batch it is
+    in (1..32 tokens): routing, expert sums and the combine are per token, in an order that
+    does not depend on the batch."""
     layer, dev, bank = moe_full
     note("moe decode determinism")
     x = dev_bf16(synth.moe_tokens(4, 3))
     a = bfq.bfp_moe_forward(dev, x)
     b = bfq.bfp_moe_forward(dev, x)
     assert torch.equal(a, b)
+    note("moe decode batch invariance")
+    x32 = dev_bf16(synth.moe_tokens(32, 4))
+    y32 = bfq.bfp_moe_forward(dev, x32).view(torch.int32)
+    for lo, hi in [(0, 1), (13, 14), (31, 32), (4, 12), (0, 16), (16, 32), (5, 7)]:
+        y = bfq.bfp_moe_forward(dev, x32[lo:hi].contiguous()).view(torch.int32)
+        assert torch.equal(y, y32[lo:hi]), f"tokens {lo}:{hi} differ from the 32-token call"
 
 
 def _prefill_check(layer, dev, bank, x, bias, sample):
