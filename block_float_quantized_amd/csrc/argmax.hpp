@@ -44,11 +44,13 @@ __device__ __forceinline__ uint64_t lane_max(uint64_t k) {
   return k;
 }
 
-constexpr int kRowThreads = 256;
+constexpr int kRowThreads = 1024;
+constexpr int kRowLoads = 8;          // independent loads in flight per thread
 
 // One workgroup per activation row: idx[i], val[i] from the row's `count` keys
 // (keys[i * count + j]), or, with FROM_VALUES, from the row's `count` fp32 values
-// (values[i * ld + j], the column being j).
+// (values[i * ld + j], the column being j). Each thread issues kRowLoads clamped loads before
+// it compares any of them.
 template <bool FROM_VALUES>
 __global__ __launch_bounds__(kRowThreads) void argmax_rows_kernel(const uint64_t* keys, const float* values,
                                                                   int64_t ld, int count, int32_t* idx,
@@ -56,9 +58,21 @@ __global__ __launch_bounds__(kRowThreads) void argmax_rows_kernel(const uint64_t
   __shared__ uint64_t part[kRowThreads / kWave];
   const int i = blockIdx.x;
   uint64_t best = kNone;
-  for (int j = threadIdx.x; j < count; j += kRowThreads) {
-    const uint64_t k = FROM_VALUES ? key_of(values[(int64_t)i * ld + j], j) : keys[(int64_t)i * count + j];
-    best = kmax(best, k);
+  for (int j0 = threadIdx.x; j0 < count; j0 += kRowThreads * kRowLoads) {
+    uint64_t k[kRowLoads];
+    float v[kRowLoads];
+#pragma unroll
+    for (int u = 0; u < kRowLoads; ++u) {
+      const int j = min(j0 + u * kRowThreads, count - 1);
+      if constexpr (FROM_VALUES) v[u] = values[(int64_t)i * ld + j];
+      else k[u] = keys[(int64_t)i * count + j];
+    }
+#pragma unroll
+    for (int u = 0; u < kRowLoads; ++u) {
+      const int j = j0 + u * kRowThreads;
+      const uint64_t kk = FROM_VALUES ? key_of(v[u], j) : k[u];
+      best = kmax(best, j < count ? kk : kNone);
+    }
   }
   best = lane_max<kWave>(best);
   if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = best;

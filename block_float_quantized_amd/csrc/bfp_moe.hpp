@@ -37,6 +37,9 @@ struct DispatchArgs {
   int32_t* tile_start;         // [n_exp + 2]: first row tile of each group, then the total
 };
 hipError_t dispatch_launch(const DispatchArgs& a, hipStream_t s);
+// Decode (m <= 32): the router logits, then top-k and dispatch in one single-workgroup kernel
+// (router_launch + dispatch_launch with one launch fewer; d.ids must be r.ids).
+hipError_t route_dispatch_launch(const RouteArgs& r, const DispatchArgs& d, hipStream_t s);
 
 // Expert-grouped skinny matmul for decode: workgroup row y picks the y-th active expert (or
 // the shared expert right after the active ones) and streams that expert's rows once for all

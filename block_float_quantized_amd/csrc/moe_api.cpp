@@ -1,5 +1,5 @@
 // C ABI of the MoE entry points: layer checks, workspace layout, and the decode pipeline
-// (route -> dispatch -> grouped gate/up + SwiGLU -> grouped down -> combine).
+// (router logits -> top-k + dispatch -> grouped gate/up + SwiGLU -> grouped down -> combine).
 #include <hip/hip_runtime.h>
 
 #include "../../include/libbfp.h"
@@ -162,8 +162,8 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, ly.ids);
   float* w = topk_w ? topk_w : at<float>(ws, ly.w);
   float* g = at<float>(ws, ly.g);
-  hipError_t e = bfp::router_launch(route_args(L, x, m, at<double>(ws, ly.logits), ids, w, g), s);
-  if (e != hipSuccess) return BFP_E_DEVICE;
+  const bfp::RouteArgs r = route_args(L, x, m, at<double>(ws, ly.logits), ids, w, g);
+  hipError_t e = hipSuccess;
   bfp::DispatchArgs d{};
   d.ids = ids; d.m = (int)m; d.top_k = L->top_k; d.n_exp = L->n_experts;
   d.counts = at<int32_t>(ws, ly.counts); d.offsets = at<int32_t>(ws, ly.offsets);
@@ -178,7 +178,12 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
     d.with_shared = shared;
     d.tile_start = at<int32_t>(ws, ly.extra);
   }
-  if ((e = bfp::dispatch_launch(d, s)) != hipSuccess) return BFP_E_DEVICE;
+  if (m > BFP_GEMM_MAX_M) {
+    if ((e = bfp::router_launch(r, s)) != hipSuccess) return BFP_E_DEVICE;
+    if ((e = bfp::dispatch_launch(d, s)) != hipSuccess) return BFP_E_DEVICE;
+  } else if ((e = bfp::route_dispatch_launch(r, d, s)) != hipSuccess) {
+    return BFP_E_DEVICE;
+  }
 
   if (m > BFP_GEMM_MAX_M) {
     bfp::PrefillArgs p{};

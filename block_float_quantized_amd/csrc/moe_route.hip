@@ -120,11 +120,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouteArgs a) {
   }
 }
 
-// One wave per token: top-k by (logit desc, expert asc), softmax weights, shared gate.
-__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.m) return;
+// One wave, token t: top-k by (logit desc, expert asc), softmax weights, shared gate. With
+// eid, the selected experts also go to eid[t * top_k + j] (LDS bytes).
+__device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, uint8_t* eid) {
   const double* l = a.logits + (int64_t)t * a.ld_logits;
   constexpr int kPer = 4;                                   // n_exp <= 256
   double v[kPer];
@@ -165,12 +163,20 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   if (lane < a.top_k) {
     a.ids[(int64_t)t * a.top_k + lane] = ej;
     a.w[(int64_t)t * a.top_k + lane] = (float)(ex / z);
+    if (eid) eid[t * a.top_k + lane] = (uint8_t)ej;
   }
   if (a.g && lane == 63) {
     float gv = 1.0f;
     if (a.sh_gate_w) gv = (float)(1.0 / (1.0 + exp(-l[a.n_exp])));
     a.g[t] = gv;
   }
+}
+
+// One wave per token.
+__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.m) return;
+  topk_token(a, t, threadIdx.x & 63, nullptr);
 }
 
 // Counting sort of the (token, slot) pairs by expert; one workgroup of 1024 threads. The
@@ -181,19 +187,37 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
 // earlier chunks.
 constexpr int kDispThreads = 1024;
 constexpr int kDispMaxPairs = 8192 * 8;          // most tokens x top_k the kernel takes
-__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(DispatchArgs a) {
-  __shared__ uint8_t eid[kDispMaxPairs];
-  __shared__ uint32_t bitmap[256][33];                      // 32 words + pad per expert
-  __shared__ int cnt[256];
-  __shared__ int off[257];
-  __shared__ int base[256];
-  __shared__ int wpre[256][33];
-  __shared__ int wtot[4][3];
+
+template <int MAXP>
+struct DispLds {
+  uint8_t eid[MAXP];                              // expert of each pair
+  uint32_t bitmap[256][33];                       // 32 words + pad per expert
+  int cnt[256];
+  int off[257];
+  int base[256];
+  int wpre[256][33];
+  int wtot[4][3];
+};
+
+// The counting sort on one workgroup of kDispThreads threads. With ids_in_lds the pairs'
+// experts are already in sh.eid (and sh.cnt is not counted yet); else they are read from a.ids.
+template <int MAXP>
+__device__ __forceinline__ void dispatch_block(const DispatchArgs& a, DispLds<MAXP>& sh, bool ids_in_lds) {
+  uint8_t* eid = sh.eid;
+  auto& bitmap = sh.bitmap;
+  int* cnt = sh.cnt;
+  int* off = sh.off;
+  int* base = sh.base;
+  auto& wpre = sh.wpre;
+  auto& wtot = sh.wtot;
   const int tid = threadIdx.x;
   const int E = a.n_exp, K = a.top_k;
   if (tid < 256) { cnt[tid] = 0; base[tid] = 0; }
   __syncthreads();
   const int np = a.m * K;
+  if (ids_in_lds) {
+    for (int p = tid; p < np; p += kDispThreads) atomicAdd(&cnt[eid[p]], 1);
+  } else {
   // ids -> LDS bytes and counts; four 16-byte loads issued before their use
   const bool vec = (reinterpret_cast<uintptr_t>(a.ids) & 15) == 0;
   const int nq = vec ? np / 4 : 0;
@@ -220,6 +244,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(DispatchArgs a) 
     const int e = a.ids[p];
     eid[p] = (uint8_t)e;
     atomicAdd(&cnt[e], 1);
+  }
   }
   __syncthreads();
   // exclusive scans over the experts (threads 0..255, one value each): pair offsets, the
@@ -305,6 +330,22 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(DispatchArgs a) 
     if (tid < E) base[tid] += wpre[tid][32];
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(DispatchArgs a) {
+  __shared__ DispLds<kDispMaxPairs> sh;
+  dispatch_block(a, sh, false);
+}
+
+// Decode (m <= 32 tokens): top-k of every token (one wave per token) and the counting sort in
+// one workgroup; the selected experts pass from the first part to the second through LDS.
+constexpr int kDecodeMaxPairs = 32 * 8;
+__global__ __launch_bounds__(kDispThreads) void topk_dispatch_kernel(RouteArgs r, DispatchArgs a) {
+  __shared__ DispLds<kDecodeMaxPairs> sh;
+  const int lane = threadIdx.x & 63;
+  for (int t = threadIdx.x >> 6; t < r.m; t += kDispThreads / 64) topk_token(r, t, lane, sh.eid);
+  __syncthreads();
+  dispatch_block(a, sh, true);
 }
 
 
@@ -635,6 +676,16 @@ hipError_t router_launch(const RouteArgs& a, hipStream_t s) {
 
 hipError_t dispatch_launch(const DispatchArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t route_dispatch_launch(const RouteArgs& r, const DispatchArgs& d, hipStream_t s) {
+  if (r.m > 32 || r.m * r.top_k > kDecodeMaxPairs) return hipErrorInvalidValue;
+  const int rows = r.n_exp + (r.sh_gate_w ? 1 : 0);
+  hipLaunchKernelGGL(router_logits_kernel, dim3((rows + 15) / 16, r.m), dim3(256), 0, s, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_dispatch_kernel, dim3(1), dim3(kDispThreads), 0, s, r, d);
   return hipGetLastError();
 }
 
