@@ -56,14 +56,17 @@ def parse():
     ap.add_argument("--pmc-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of --pmc-driver "
                          "into the traffic summary")
+    ap.add_argument("--kernel-summary", metavar="TRACE_DIR",
+                    help="turn a rocprofv3 --kernel-trace output folder into a per-kernel markdown table")
     return ap.parse_args()
 
 
 # ---- HBM traffic of the headline kernel (rocprofv3 counters) ------------------------------
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_bfp4_gateup_m1_hbm_traffic.md")
-HEADLINE_SOURCES = ("block_float_quantized_amd/csrc/gemv_impl.hpp", "block_float_quantized_amd/csrc/gemv_b4_bf16x.hip",
-                    "block_float_quantized_amd/csrc/bfp_device.hpp", "block_float_quantized_amd/csrc/gemv.hip")
+# the headline kernel's translation unit and every header it includes
+HEADLINE_SOURCES = tuple(f"block_float_quantized_amd/csrc/{f}" for f in (
+    "gemv_b4_bf16x.hip", "gemv_impl.hpp", "bfp_device.hpp", "bfp_internal.hpp", "argmax.hpp"))
 HEADLINE_KERNEL = "gemv_kernel<4, 1, 1, 16, 2, 2, 2, true, 256, false>"
 COPY_BYTES = 512 << 20
 
@@ -145,6 +148,41 @@ def pmc_report(fetch_dir: str, write_dir: str):
     print(f"scaled HBM bytes per launch: read {fetch_b:.0f}, written {write_b:.0f}; algorithmic {alg}")
     print(f"traffic_bytes_per_launch: {int(round(fetch_b + write_b))}")
     print(f"kernel_sources_sha256: {headline_sources_sha256()}")
+
+
+def short_kernel_name(name: str) -> str:
+    """Kernel name without return type, namespaces and parameter list (template arguments kept)."""
+    import re
+    n = name[5:] if name.startswith("void ") else name
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):           # drop the parameter list: the last '(' at template depth 0
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not n.startswith("(anonymous", i):
+            cut = i
+    n = n[:cut]
+    n = re.sub(r"\(anonymous namespace\)::", "", n)
+    n = re.sub(r"\b(bfp|at::native|std|gemv_detail|mg|am)::", "", n)
+    return n
+
+
+def kernel_summary(trace_dir: str):
+    """Per-kernel call count, average / min / max duration and share of kernel time."""
+    import glob
+    import sqlite3
+    db = glob.glob(os.path.join(trace_dir, "**", "*.db"), recursive=True)[0]
+    rows = sqlite3.connect(db).execute("select name, start, end from kernels").fetchall()
+    acc = {}
+    for name, t0, t1 in rows:
+        acc.setdefault(short_kernel_name(name), []).append((t1 - t0) / 1000.0)
+    total = sum(sum(v) for v in acc.values())
+    print("| kernel | calls | avg (us) | min (us) | max (us) | share |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for k, v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{k}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+              f"{100 * sum(v) / total:.1f}% |")
 
 
 def log(msg):
@@ -371,6 +409,9 @@ def moe_workloads(args):
 
 def main():
     args = parse()
+    if args.kernel_summary:
+        kernel_summary(args.kernel_summary)
+        return
     if args.pmc_report:
         pmc_report(*args.pmc_report)
         return
