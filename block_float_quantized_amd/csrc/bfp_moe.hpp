@@ -35,7 +35,10 @@ struct DispatchArgs {
   int tile_m;                  // > 0: also write tile_start for row tiles of tile_m rows
   int with_shared;             // the tile list ends with a group of all m tokens
   int32_t* tile_start;         // [n_exp + 2]: first row tile of each group, then the total
+  int32_t* chunk_counts;       // dispatch_scratch_bytes(m) of scratch: many-token sort over several
+                               // workgroups; null: one workgroup
 };
+size_t dispatch_scratch_bytes(int m);
 hipError_t dispatch_launch(const DispatchArgs& a, hipStream_t s);
 // Decode (m <= 32): the router logits, then top-k and dispatch in one single-workgroup kernel
 // (router_launch + dispatch_launch with one launch fewer; d.ids must be r.ids).

@@ -46,7 +46,7 @@ int32_t check_layer(const bfp_moe_layer* L) {
 
 // Workspace regions, each 256-byte aligned.
 struct Layout {
-  size_t logits, ids, w, g, counts, offsets, perm, inv, active, nact, h, o, extra, total;
+  size_t logits, ids, w, g, counts, offsets, perm, inv, active, nact, chunks, h, o, extra, total;
 };
 
 size_t place(size_t& off, size_t bytes) {
@@ -73,6 +73,7 @@ Layout layout(const bfp_moe_layer* L, int64_t m, bool with_experts) {
     y.active = place(off, (size_t)E * 4);
     y.nact = place(off, 16);
     if (prefill) {
+      y.chunks = place(off, bfp::dispatch_scratch_bytes((int)m));
       y.h = place(off, (size_t)pairs * F * 2);       // bf16 h
       y.o = place(off, (size_t)pairs * H * 4);
       y.extra = off;
@@ -173,6 +174,7 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
     d.tile_m = bfp::prefill_tile_rows();
     d.with_shared = shared;
     d.tile_start = at<int32_t>(ws, ly.extra);
+    d.chunk_counts = at<int32_t>(ws, ly.chunks);
   } else if (m > 1) {
     d.tile_m = bfp::kDecodeTileRows;
     d.with_shared = shared;

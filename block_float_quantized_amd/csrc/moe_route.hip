@@ -188,6 +188,56 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
 constexpr int kDispThreads = 1024;
 constexpr int kDispMaxPairs = 8192 * 8;          // most tokens x top_k the kernel takes
 
+// Exclusive scans over the experts of a workgroup's counts cnt[0..n_exp) (threads 0..255 one
+// value each; every thread of the workgroup calls it): pair offsets into off[0..n_exp], and,
+// with lists, the active-expert list, its length and the first row tile of each active
+// expert's group (plus the shared group's and the total) to global memory.
+__device__ __forceinline__ void expert_scan(const DispatchArgs& a, const int* cnt, int* off, int (*wtot)[3],
+                                            bool lists) {
+  const int tid = threadIdx.x;
+  const int E = a.n_exp;
+  {
+    const int c = (tid < E) ? cnt[tid] : 0;
+    const int act = c > 0 ? 1 : 0;
+    const int tl = (a.tile_m > 0 && c > 0) ? (c + a.tile_m - 1) / a.tile_m : 0;
+    int3 v = make_int3(c, act, tl);
+    int3 inc = v;
+    if (tid < 256) {
+      const int lane = tid & 63;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int x0 = __shfl_up(inc.x, o), x1 = __shfl_up(inc.y, o), x2 = __shfl_up(inc.z, o);
+        if (lane >= o) { inc.x += x0; inc.y += x1; inc.z += x2; }
+      }
+      if (lane == 63) { wtot[tid >> 6][0] = inc.x; wtot[tid >> 6][1] = inc.y; wtot[tid >> 6][2] = inc.z; }
+    }
+    __syncthreads();
+    if (tid < 256) {
+      int3 base3 = make_int3(0, 0, 0);
+      for (int w = 0; w < (tid >> 6); ++w) { base3.x += wtot[w][0]; base3.y += wtot[w][1]; base3.z += wtot[w][2]; }
+      const int ex_off = base3.x + inc.x - v.x;
+      const int ex_act = base3.y + inc.y - v.y;
+      const int ex_til = base3.z + inc.z - v.z;
+      if (tid < E) {
+        off[tid] = ex_off;
+        if (act && lists && a.active) a.active[ex_act] = tid;
+        if (act && lists && a.tile_m > 0) a.tile_start[ex_act] = ex_til;
+      }
+      if (tid == 255) {
+        const int tot_pairs = base3.x + inc.x, na = base3.y + inc.y, tiles = base3.z + inc.z;
+        off[E] = tot_pairs;
+        if (lists && a.n_active) *a.n_active = na;
+        if (lists && a.tile_m > 0) {
+          int ts = tiles, g = na;
+          if (a.with_shared) { a.tile_start[g++] = ts; ts += (a.m + a.tile_m - 1) / a.tile_m; }
+          a.tile_start[g] = ts;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
 template <int MAXP>
 struct DispLds {
   uint8_t eid[MAXP];                              // expert of each pair
@@ -247,48 +297,7 @@ __device__ __forceinline__ void dispatch_block(const DispatchArgs& a, DispLds<MA
   }
   }
   __syncthreads();
-  // exclusive scans over the experts (threads 0..255, one value each): pair offsets, the
-  // rank of each active expert, and the first row tile of each active expert's group
-  {
-    const int c = (tid < E) ? cnt[tid] : 0;
-    const int act = c > 0 ? 1 : 0;
-    const int tl = (a.tile_m > 0 && c > 0) ? (c + a.tile_m - 1) / a.tile_m : 0;
-    int3 v = make_int3(c, act, tl);
-    int3 inc = v;
-    if (tid < 256) {
-      const int lane = tid & 63;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int x0 = __shfl_up(inc.x, o), x1 = __shfl_up(inc.y, o), x2 = __shfl_up(inc.z, o);
-        if (lane >= o) { inc.x += x0; inc.y += x1; inc.z += x2; }
-      }
-      if (lane == 63) { wtot[tid >> 6][0] = inc.x; wtot[tid >> 6][1] = inc.y; wtot[tid >> 6][2] = inc.z; }
-    }
-    __syncthreads();
-    if (tid < 256) {
-      int3 base3 = make_int3(0, 0, 0);
-      for (int w = 0; w < (tid >> 6); ++w) { base3.x += wtot[w][0]; base3.y += wtot[w][1]; base3.z += wtot[w][2]; }
-      const int ex_off = base3.x + inc.x - v.x;
-      const int ex_act = base3.y + inc.y - v.y;
-      const int ex_til = base3.z + inc.z - v.z;
-      if (tid < E) {
-        off[tid] = ex_off;
-        if (act && a.active) a.active[ex_act] = tid;
-        if (act && a.tile_m > 0) a.tile_start[ex_act] = ex_til;
-      }
-      if (tid == 255) {
-        const int tot_pairs = base3.x + inc.x, na = base3.y + inc.y, tiles = base3.z + inc.z;
-        off[E] = tot_pairs;
-        if (a.n_active) *a.n_active = na;
-        if (a.tile_m > 0) {
-          int ts = tiles, g = na;
-          if (a.with_shared) { a.tile_start[g++] = ts; ts += (a.m + a.tile_m - 1) / a.tile_m; }
-          a.tile_start[g] = ts;
-        }
-      }
-    }
-  }
-  __syncthreads();
+  expert_scan(a, cnt, off, wtot, true);
   if (tid < E) a.counts[tid] = cnt[tid];
   if (tid <= E) a.offsets[tid] = off[tid];
   for (int c0 = 0; c0 < a.m; c0 += kDispThreads) {
@@ -346,6 +355,77 @@ __global__ __launch_bounds__(kDispThreads) void topk_dispatch_kernel(RouteArgs r
   for (int t = threadIdx.x >> 6; t < r.m; t += kDispThreads / 64) topk_token(r, t, lane, sh.eid);
   __syncthreads();
   dispatch_block(a, sh, true);
+}
+
+// Many tokens: the same counting sort over several workgroups, with the same result. Chunk g
+// holds tokens [g C, (g + 1) C). dispatch_count_kernel: workgroup g counts the experts of its
+// chunk into chunk_counts[g][0..256). dispatch_scatter_kernel: workgroup g adds, per expert,
+// the counts of the chunks before its own and of all chunks, ranks its own pairs by token
+// inside each expert (LDS bitmap of the chunk's tokens) and writes their perm and inv entries;
+// workgroup 0 also writes counts, offsets and the lists.
+constexpr int kChunkTokens = 128;                 // kChunkTokens x top_k <= kDispThreads
+__global__ __launch_bounds__(kDispThreads) void dispatch_count_kernel(DispatchArgs a, int32_t* chunk_counts) {
+  __shared__ int cnt[256];
+  const int tid = threadIdx.x, g = blockIdx.x;
+  const int t0 = g * kChunkTokens;
+  const int np = min(kChunkTokens, a.m - t0) * a.top_k;
+  if (tid < 256) cnt[tid] = 0;
+  __syncthreads();
+  if (tid < np) atomicAdd(&cnt[a.ids[(int64_t)t0 * a.top_k + tid]], 1);
+  __syncthreads();
+  if (tid < 256) chunk_counts[(int64_t)g * 256 + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_scatter_kernel(DispatchArgs a, const int32_t* chunk_counts,
+                                                                        int nchunks) {
+  __shared__ int before[4][256], all[4][256];
+  __shared__ int tot[256], pre[256], off[257];
+  __shared__ int wtot[4][3];
+  __shared__ uint32_t bitmap[256][kChunkTokens / 32];
+  __shared__ uint8_t eid[kChunkTokens * 8];
+  const int tid = threadIdx.x, g = blockIdx.x;
+  const int K = a.top_k;
+  {
+    // four threads per expert, each over a quarter of the chunks
+    const int e = tid & 255, q = tid >> 8;
+    int sb = 0, sa = 0;
+    for (int c = q; c < nchunks; c += 4) {
+      const int v = chunk_counts[(int64_t)c * 256 + e];
+      sa += v;
+      if (c < g) sb += v;
+    }
+    before[q][e] = sb;
+    all[q][e] = sa;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    pre[tid] = before[0][tid] + before[1][tid] + before[2][tid] + before[3][tid];
+    tot[tid] = all[0][tid] + all[1][tid] + all[2][tid] + all[3][tid];
+  }
+  if (tid < 256 * (kChunkTokens / 32)) bitmap[tid / (kChunkTokens / 32)][tid % (kChunkTokens / 32)] = 0;
+  __syncthreads();
+  expert_scan(a, tot, off, wtot, g == 0);
+  if (g == 0) {
+    if (tid < a.n_exp) a.counts[tid] = tot[tid];
+    if (tid <= a.n_exp) a.offsets[tid] = off[tid];
+  }
+  const int t0 = g * kChunkTokens;
+  const int np = min(kChunkTokens, a.m - t0) * K;
+  const int tl = tid / K;
+  if (tid < np) {
+    const int e = a.ids[(int64_t)t0 * K + tid];
+    eid[tid] = (uint8_t)e;
+    atomicOr(&bitmap[e][tl / 32], 1u << (tl % 32));
+  }
+  __syncthreads();
+  if (tid < np) {
+    const int e = eid[tid];
+    int rank = __popc(bitmap[e][tl / 32] & ((1u << (tl % 32)) - 1u));
+    for (int w = 0; w < tl / 32; ++w) rank += __popc(bitmap[e][w]);
+    const int pos = off[e] + pre[e] + rank;
+    a.perm[pos] = t0 * K + tid;
+    if (a.inv) a.inv[t0 * K + tid] = pos;
+  }
 }
 
 
@@ -674,7 +754,17 @@ hipError_t router_launch(const RouteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+size_t dispatch_scratch_bytes(int m) { return (size_t)((m + kChunkTokens - 1) / kChunkTokens) * 256 * sizeof(int32_t); }
+
 hipError_t dispatch_launch(const DispatchArgs& a, hipStream_t s) {
+  if (a.chunk_counts != nullptr && a.m > kChunkTokens) {
+    const int nchunks = (a.m + kChunkTokens - 1) / kChunkTokens;
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kDispThreads), 0, s, a, a.chunk_counts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nchunks), dim3(kDispThreads), 0, s, a, a.chunk_counts, nchunks);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -166,6 +166,23 @@ def test_moe_prefill_small(moe_full):
     _prefill_check(layer, dev, bank, x, None, np.arange(40))
 
 
+@pytest.mark.parametrize("crowded", [False, True])
+def test_moe_prefill_multi_chunk_dispatch(moe_full, crowded):
+    """300 tokens: the many-token dispatch runs over three token chunks (128, 128, 44), so each
+    expert's pairs are ranked across chunks; with crowded experts (a +40 bias on eight
+    experts) every chunk feeds the same groups. Every token is checked."""
+    layer, dev, bank = moe_full
+    note(f"moe prefill m=300 crowded={crowded}")
+    bias = None
+    devb = dev
+    if crowded:
+        bias = np.zeros(256, dtype=np.float32)
+        bias[[3, 17, 42, 64, 99, 128, 200, 255]] = 40.0
+        devb = bfq.MoeLayer(**{**dev.__dict__, "router_bias": dev_f32(bias)})
+    x = synth.moe_tokens(300, 21)
+    _prefill_check(layer, devb, bank, x, bias, np.arange(300))
+
+
 def test_moe_prefill_chunk_2048(moe_full):
     """The 2,048-token prefill chunk with a skewed N(0, 1.5) per-expert router bias."""
     layer, dev, bank = moe_full
