@@ -26,13 +26,15 @@ signed zero, subnormals, the byte layout, where activations are rounded), the or
 takes one stated reading; each function says which.
 
 Modules: ``bfp`` (encode/decode/storage sizes), ``linalg`` (bf16 rounding, GEMM,
-SwiGLU, greedy pick, error normaliser), ``moe`` (router, top-k, decode and prefill MoE, dispatch).
+SwiGLU, greedy pick, error normaliser), ``moe`` (router, top-k, decode and prefill MoE, dispatch),
+``attn`` (BFP8 KV cache rows, single-token decode attention).
 Every function here is pinned by ``tests/test_oracle_*.py`` against hand-worked values,
 brute force, exact rational arithmetic, invariants or byte counts printed on the pages.
 """
-from . import bfp, linalg, moe  # noqa: F401
+from . import attn, bfp, linalg, moe  # noqa: F401
 from .bfp import (BFP4, BFP8, NonFiniteError, code_bytes, decode, encode, exp_bytes,  # noqa: F401
                   mantissa_bits, storage_bytes, unpack_codes)
 from .linalg import (bf16_round, bf16_to_f64, gemm, greedy_pick, normaliser, rel_err, silu,  # noqa: F401
                      swiglu)
 from .moe import dispatch, moe_decode, moe_prefill, route  # noqa: F401
+from .attn import decode_attention, kv_decode, kv_encode  # noqa: F401

@@ -1,0 +1,82 @@
+"""Pins for the oracle's KV-cache encoding and decode attention (CPU only)."""
+import math
+
+import numpy as np
+
+import oracle
+from oracle import BFP8
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def test_kv_encode_is_the_weight_encoding_per_row():
+    # the cache layout is [kv_head][token][...]: row (h, t) is token t of head h
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 2, 32)).astype(np.float32)
+    exp, code = oracle.kv_encode(x)
+    assert exp.shape == (2, 5, 2) and code.shape == (2, 5, 32)
+    for h in range(2):
+        for t in range(5):
+            e1, c1 = oracle.encode(x[t, h][None, :], BFP8)
+            assert np.array_equal(exp[h, t], e1[0]) and np.array_equal(code[h, t], c1[0])
+    back = oracle.kv_decode(exp, code, BFP8, 32)
+    assert back.shape == (2, 5, 32)
+    # decoded entries are within half a step of the inputs (steps are 2^(E-133) for BFP8)
+    assert np.all(np.abs(back.transpose(1, 0, 2) - x) <= np.abs(x).max() * 2.0 ** -7)
+
+
+def test_attention_one_token_returns_its_value():
+    rng = np.random.default_rng(1)
+    q, k, v = _rand(rng, 4, 16), _rand(rng, 2, 1, 16), _rand(rng, 2, 1, 16)
+    out, norm = oracle.decode_attention(q, k, v, 0.25)
+    assert np.array_equal(out, v[np.arange(4) // 2, 0])
+    assert np.array_equal(norm, np.abs(v[np.arange(4) // 2, 0]))
+
+
+def test_attention_equal_scores_average_the_values():
+    rng = np.random.default_rng(2)
+    k, v = _rand(rng, 1, 6, 8), _rand(rng, 1, 6, 8)
+    out, _ = oracle.decode_attention(np.zeros((3, 8)), k, v, 1.0)
+    assert np.allclose(out, v[0].mean(axis=0), rtol=0, atol=1e-15)
+
+
+def test_attention_two_tokens_closed_form():
+    # p_0 = 1 / (1 + e^(s1 - s0)) with s = scale q.k
+    q = np.array([[1.0, 2.0]])
+    k = np.array([[[0.5, 0.25], [-1.0, 0.5]]])
+    v = np.array([[[3.0, -1.0], [1.0, 5.0]]])
+    s0, s1 = 0.7 * (0.5 + 0.5), 0.7 * (-1.0 + 1.0)
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    out, _ = oracle.decode_attention(q, k, v, 0.7)
+    assert np.allclose(out[0], p0 * v[0, 0] + (1 - p0) * v[0, 1], rtol=1e-15, atol=0)
+
+
+def test_attention_groups_queries_onto_kv_heads():
+    # KV head g holds constant values g + 1: query head h must return h // group + 1
+    rng = np.random.default_rng(3)
+    hkv, group, L, d = 3, 4, 5, 8
+    k = _rand(rng, hkv, L, d)
+    v = np.broadcast_to((np.arange(hkv) + 1.0)[:, None, None], (hkv, L, d))
+    out, _ = oracle.decode_attention(_rand(rng, hkv * group, d), k, v, 0.3)
+    assert np.allclose(out, (np.arange(hkv * group) // group + 1.0)[:, None], rtol=1e-14, atol=0)
+
+
+def test_attention_token_order_does_not_matter_and_scale_folds_into_q():
+    rng = np.random.default_rng(4)
+    q, k, v = _rand(rng, 2, 16), _rand(rng, 1, 9, 16), _rand(rng, 1, 9, 16)
+    perm = rng.permutation(9)
+    a, _ = oracle.decode_attention(q, k, v, 0.2)
+    b, _ = oracle.decode_attention(q, k[:, perm], v[:, perm], 0.2)
+    c, _ = oracle.decode_attention(0.2 * q, k, v, 1.0)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15) and np.allclose(a, c, rtol=1e-13, atol=1e-15)
+
+
+def test_attention_large_scores_do_not_overflow_and_pick_the_maximum():
+    # one score far above the rest: the output is that token's value (softmax is shift-free)
+    q = np.array([[100.0, 0.0]])
+    k = np.array([[[10.0, 0.0], [9.0, 0.0], [-10.0, 0.0]]])
+    v = np.array([[[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]]])
+    out, _ = oracle.decode_attention(q, k, v, 1.0)
+    assert np.all(np.isfinite(out)) and np.allclose(out[0], [1.0, 2.0], rtol=0, atol=1e-40)
