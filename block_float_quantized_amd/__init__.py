@@ -6,7 +6,7 @@ provides device memory and streams. There is no CPU fallback: if ``libbfp.so`` i
 fails to load, every call raises.
 
 Functions keep the C names (``bfp_quantize``, ``bfp_dequantize``, ``bfp_gemm``,
-``bfp_gemm_argmax``, ``bfp_moe_route``, ``bfp_moe_dispatch``, ``bfp_moe_workspace_bytes``, ``bfp_moe_forward``)
+``bfp_gemm_argmax``, ``bfp_kv_append``, ``bfp_attn_decode``, ``bfp_moe_route``, ``bfp_moe_dispatch``, ``bfp_moe_workspace_bytes``, ``bfp_moe_forward``)
 and take torch tensors where the C call takes device pointers.
 """
 from __future__ import annotations
@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "BFP4", "BFP8", "BfpError", "BfpMatrix", "MoeLayer", "lib", "library_path",
     "bfp_quantize", "bfp_dequantize", "bfp_gemm", "bfp_gemm_workspace_bytes", "bfp_gemm_argmax",
-    "bfp_gemm_argmax_workspace_bytes", "bfp_moe_route", "bfp_moe_dispatch",
+    "bfp_gemm_argmax_workspace_bytes", "bfp_moe_route", "bfp_moe_dispatch", "KvCache", "bfp_kv_append",
+    "bfp_attn_decode", "bfp_attn_decode_workspace_bytes",
     "bfp_moe_workspace_bytes", "bfp_moe_forward", "exp_bytes", "code_bytes",
 ]
 
@@ -59,6 +60,12 @@ class _MoeLayer(ctypes.Structure):
                 ("sh_gate_w", ctypes.c_void_p)]
 
 
+class _KvCache(ctypes.Structure):
+    _fields_ = [("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int64),
+                ("k_exp", ctypes.c_void_p), ("k_code", ctypes.c_void_p), ("v_exp", ctypes.c_void_p),
+                ("v_code", ctypes.c_void_p)]
+
+
 _LIB = None
 
 # name -> (restype, argtypes)
@@ -81,6 +88,12 @@ _SIGS = {
     "bfp_gemm_argmax": (ctypes.c_int32, [ctypes.POINTER(_Tensor), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "bfp_kv_append": (ctypes.c_int32, [ctypes.POINTER(_KvCache), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "bfp_attn_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_KvCache), ctypes.c_int32, ctypes.c_int64]),
+    "bfp_attn_decode": (ctypes.c_int32, [ctypes.POINTER(_KvCache), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]),
     "bfp_moe_route_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_MoeLayer), ctypes.c_int64]),
     "bfp_moe_route": (ctypes.c_int32, [ctypes.POINTER(_MoeLayer), ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -255,6 +268,63 @@ def bfp_gemm_argmax(w: BfpMatrix, x: torch.Tensor, idx: torch.Tensor | None = No
                                _ptr(workspace), workspace.numel(), _stream(stream))
     _check("bfp_gemm_argmax", st)
     return idx, val
+
+
+@dataclass
+class KvCache:
+    """A BFP8 KV cache in device memory (see bfp_kv_cache in include/libbfp.h)."""
+    kv_heads: int
+    head_dim: int
+    max_tokens: int
+    k_exp: torch.Tensor
+    k_code: torch.Tensor
+    v_exp: torch.Tensor
+    v_code: torch.Tensor
+
+    @staticmethod
+    def empty(kv_heads: int, head_dim: int, max_tokens: int, device="cuda") -> "KvCache":
+        rows = kv_heads * max_tokens
+        ne, nc = exp_bytes(rows, head_dim), code_bytes(BFP8, rows, head_dim)
+        z = lambda n: torch.zeros((n,), dtype=torch.uint8, device=device)
+        return KvCache(kv_heads, head_dim, max_tokens, z(ne), z(nc), z(ne), z(nc))
+
+    def view(self) -> _KvCache:
+        return _KvCache(self.kv_heads, self.head_dim, self.max_tokens, _ptr(self.k_exp), _ptr(self.k_code),
+                        _ptr(self.v_exp), _ptr(self.v_code))
+
+    @property
+    def nbytes(self) -> int:
+        return self.k_exp.numel() + self.k_code.numel() + self.v_exp.numel() + self.v_code.numel()
+
+
+def bfp_kv_append(cache: KvCache, k: torch.Tensor, v: torch.Tensor, pos: int, stream=None) -> None:
+    """Encode k, v ([n][kv_heads][head_dim], fp32 or bf16) into token slots pos .. pos + n - 1."""
+    if k.shape != v.shape or k.dtype != v.dtype or not (k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("k and v must be contiguous [n][kv_heads][head_dim] tensors of one dtype")
+    st = lib().bfp_kv_append(ctypes.byref(cache.view()), _ptr(k), _ptr(v), _dt(k), pos, k.shape[0], _stream(stream))
+    _check("bfp_kv_append", st)
+
+
+def bfp_attn_decode_workspace_bytes(cache: KvCache, q_heads: int, seq_len: int) -> int:
+    return int(lib().bfp_attn_decode_workspace_bytes(ctypes.byref(cache.view()), q_heads, seq_len))
+
+
+def bfp_attn_decode(cache: KvCache, q: torch.Tensor, seq_len: int, scale: float, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Single-token attention of q ([q_heads][head_dim], fp32 or bf16) over the first seq_len
+    cached tokens; returns fp32 [q_heads][head_dim]."""
+    if q.dim() != 2 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [q_heads][head_dim] tensor")
+    hq = q.shape[0]
+    if out is None:
+        out = torch.empty((hq, cache.head_dim), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = bfp_attn_decode_workspace_bytes(cache, hq, seq_len)
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    st = lib().bfp_attn_decode(ctypes.byref(cache.view()), _ptr(q), _dt(q), hq, seq_len, float(scale), _ptr(out),
+                               _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("bfp_attn_decode", st)
+    return out
 
 
 @dataclass

@@ -242,6 +242,50 @@ int32_t bfp_moe_forward(const bfp_moe_layer *L, const uint16_t *x, int64_t m, fl
                         int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
                         void *stream);
 
+/*
+ * BFP8 KV cache for decode attention ("Qwen3.6-35B-A3B ...", "Precision as served": the KV
+ * cache is BFP8; serving-settings table, KV-precision row: BFP8 halves the cache, 20.0 ->
+ * 10.6 KiB per token, and decode attention, which reads the whole cache every step, gets
+ * faster at long contexts). Every cached key or value vector (one token, one KV head,
+ * head_dim values) is a BFP8 row encoded exactly as bfp_quantize encodes a weight row.
+ * Layout (device memory owned by the caller), for K and for V alike:
+ *   exp  : uint8 [kv_heads][max_tokens][head_dim/16]  (bfp_exp_bytes(kv_heads*max_tokens, head_dim))
+ *   code : uint8 [kv_heads][max_tokens][head_dim]     (bfp_code_bytes(BFP_FMT_BFP8, ...))
+ */
+typedef struct bfp_kv_cache {
+  int32_t kv_heads;       /* 1..64 */
+  int32_t head_dim;       /* 64, 128 or 256 */
+  int64_t max_tokens;     /* token slots, 1..2^24 */
+  uint8_t *k_exp, *k_code, *v_exp, *v_code;
+} bfp_kv_cache;
+
+/*
+ * Encode n new tokens into slots pos .. pos+n-1 of every KV head. k, v: device
+ * [n][kv_heads][head_dim] of dtype (fp32, or bf16 converted exactly). Inputs must be finite
+ * (Inf/NaN leave unspecified codes; no synchronisation, unlike bfp_quantize). pos + n must
+ * not exceed max_tokens.
+ */
+int32_t bfp_kv_append(const bfp_kv_cache *c, const void *k, const void *v, int32_t dtype,
+                      int64_t pos, int64_t n, void *stream);
+
+/* Workspace bytes of bfp_attn_decode (0 if the arguments are invalid). */
+size_t bfp_attn_decode_workspace_bytes(const bfp_kv_cache *c, int32_t q_heads, int64_t seq_len);
+
+/*
+ * Single-token decode attention over the first seq_len cached tokens, for one sequence:
+ *   query head h reads KV head h / (q_heads / kv_heads);
+ *   s_t = scale * q[h] . K[t] (decoded keys), p = softmax over t < seq_len,
+ *   out[h] = sum_t p_t V[t] (decoded values).
+ * q: device [q_heads][head_dim], fp32 or bf16 (q_dtype); out: device fp32
+ * [q_heads][head_dim]. q_heads / kv_heads must be 1, 2, 4 or 8 (else BFP_E_UNSUPPORTED).
+ * Products and sums are fp32 (exp via the hardware exp2); the sequence is split into chunks
+ * merged in a fixed order, so results are deterministic. ws: device workspace of at least
+ * bfp_attn_decode_workspace_bytes bytes.
+ */
+int32_t bfp_attn_decode(const bfp_kv_cache *c, const void *q, int32_t q_dtype, int32_t q_heads,
+                        int64_t seq_len, float scale, float *out, void *ws, size_t ws_bytes,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

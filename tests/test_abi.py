@@ -102,6 +102,24 @@ def test_host_validation_before_any_launch():
     assert lib.bfp_gemm_workspace_bytes(ctypes.byref(big), None, 1) > 0
 
 
+def test_kv_cache_host_validation():
+    lib = bfq.lib()
+    c = bfq._KvCache(2, 256, 100, 16, 16, 16, 16)
+    assert lib.bfp_kv_append(ctypes.byref(c), 16, 16, 0, 90, 11, None) == 2                   # past the slots
+    assert lib.bfp_kv_append(ctypes.byref(c), 16, 16, 5, 0, 1, None) == 1                     # bad dtype
+    assert lib.bfp_kv_append(ctypes.byref(c), 24, 16, 0, 0, 1, None) == 3                    # misaligned k
+    bad = bfq._KvCache(2, 96, 100, 16, 16, 16, 16)
+    assert lib.bfp_kv_append(ctypes.byref(bad), 16, 16, 0, 0, 1, None) == 2                   # head_dim
+    need = lib.bfp_attn_decode_workspace_bytes(ctypes.byref(c), 16, 100)
+    assert need > 0 and lib.bfp_attn_decode_workspace_bytes(ctypes.byref(c), 16, 101) == 0
+    assert lib.bfp_attn_decode(ctypes.byref(c), 16, 0, 16, 0, 1.0, 16, 16, need, None) == 2   # seq_len 0
+    assert lib.bfp_attn_decode(ctypes.byref(c), 16, 0, 6, 10, 1.0, 16, 16, need, None) == 7   # group 3
+    assert lib.bfp_attn_decode(ctypes.byref(c), 16, 0, 5, 10, 1.0, 16, 16, need, None) == 2   # not a multiple
+    assert lib.bfp_attn_decode(ctypes.byref(c), 16, 0, 16, 100, 1.0, 16, 16, need - 1, None) == 5
+    assert lib.bfp_attn_decode(ctypes.byref(c), 16, 0, 16, 100, float("nan"), 16, 16, need, None) == 1
+    assert lib.bfp_attn_decode(ctypes.byref(c), 16, 0, 16, 100, 1.0, 20, 16, need, None) == 3  # misaligned out
+
+
 def test_python_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(bfq, "_LIB", None)
     monkeypatch.setattr(bfq, "library_path", lambda: str(tmp_path / "missing.so"))
