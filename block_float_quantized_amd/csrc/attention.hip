@@ -250,20 +250,23 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(ChunkArgs ca) 
   }
 }
 
-// One workgroup per query head: merge the chunks. The maximum M of the chunk maxima first;
-// then kMergeGroups thread groups (one thread per dimension) each add a fixed residue class of
-// chunks in chunk order, eight chunks' loads in flight per thread, and the groups' sums are
-// added in group order: the result does not depend on scheduling.
+// Workgroup (h, j): dimensions [64 j, 64 j + 64) of query head h, merged over the chunks. The
+// maximum M of the chunk maxima first; then kMergeGroups thread groups (one thread per
+// dimension) each add a fixed residue class of chunks in chunk order, eight chunks' loads in
+// flight per thread, and the groups' sums are added in group order: the result does not
+// depend on scheduling.
 constexpr int kMergeThreads = 1024;
-constexpr int kMergeGroups = 4;
+constexpr int kMergeDims = 64;
+constexpr int kMergeGroups = kMergeThreads / kMergeDims;
 template <int HD>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(ChunkArgs ca) {
-  constexpr int GT = kMergeThreads / kMergeGroups;   // threads per group (>= HD)
+  constexpr int GT = kMergeDims;                     // threads per group
   constexpr int U = 8;
   __shared__ float wmax[kMergeThreads / kWave];
-  __shared__ float po[kMergeGroups][HD], pl[kMergeGroups];
+  __shared__ float po[kMergeGroups][GT], pl[kMergeGroups];
   const AttnArgs& a = ca.a;
   const int h = blockIdx.x, tid = threadIdx.x;
+  const int d0 = blockIdx.y * kMergeDims;
   const float* ml = a.ws + (int64_t)ca.nchunks * a.q_heads * HD;
   float mx = -__builtin_inff();
   for (int c = tid; c < ca.nchunks; c += kMergeThreads) mx = fmaxf(mx, ml[((int64_t)c * a.q_heads + h) * 2]);
@@ -273,9 +276,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(ChunkArgs ca)
   mx = wmax[0];
 #pragma unroll
   for (int w = 1; w < kMergeThreads / kWave; ++w) mx = fmaxf(mx, wmax[w]);
-  const int grp = tid / GT, d = tid % GT;
+  const int grp = tid / GT, d = d0 + tid % GT;
   float l = 0.f, o = 0.f;
-  if (d < HD) {
+  {
     for (int c0 = grp; c0 < ca.nchunks; c0 += kMergeGroups * U) {
       float m[U], lv[U], ov[U];
 #pragma unroll
@@ -293,18 +296,18 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(ChunkArgs ca)
         o = __builtin_fmaf(w, ov[u], o);
       }
     }
-    po[grp][d] = o;
-    if (d == 0) pl[grp] = l;
+    po[grp][tid % GT] = o;
+    if (tid % GT == 0) pl[grp] = l;
   }
   __syncthreads();
-  if (tid < HD) {
+  if (tid < GT) {
     float os = po[0][tid], ls = pl[0];
 #pragma unroll
     for (int j = 1; j < kMergeGroups; ++j) {
       os += po[j][tid];
       ls += pl[j];
     }
-    a.out[(int64_t)h * HD + tid] = os / ls;
+    a.out[(int64_t)h * HD + d0 + tid] = os / ls;
   }
 }
 
@@ -328,7 +331,7 @@ hipError_t launch_hd_g(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((attn_chunk_kernel<HD, G>), dim3(ca.nchunks, a.kv_heads), dim3(kAttnThreads), 0, s, ca);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(a.q_heads), dim3(kMergeThreads), 0, s, ca);
+  hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(a.q_heads, HD / kMergeDims), dim3(kMergeThreads), 0, s, ca);
   return hipGetLastError();
 }
 
