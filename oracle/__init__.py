@@ -27,7 +27,7 @@ takes one stated reading; each function says which.
 
 Modules: ``bfp`` (encode/decode/storage sizes), ``linalg`` (bf16 rounding, GEMM,
 SwiGLU, greedy pick, error normaliser), ``moe`` (router, top-k, decode and prefill MoE, dispatch),
-``attn`` (BFP8 KV cache rows, single-token decode attention).
+``attn`` (BFP8 KV cache rows, the rotated 4-bit V, single-token decode attention).
 Every function here is pinned by ``tests/test_oracle_*.py`` against hand-worked values,
 brute force, exact rational arithmetic, invariants or byte counts printed on the pages.
 """
@@ -37,4 +37,4 @@ from .bfp import (BFP4, BFP8, NonFiniteError, code_bytes, decode, encode, exp_by
 from .linalg import (bf16_round, bf16_to_f64, gemm, greedy_pick, normaliser, rel_err, silu,  # noqa: F401
                      swiglu)
 from .moe import dispatch, moe_decode, moe_prefill, route  # noqa: F401
-from .attn import decode_attention, kv_decode, kv_encode  # noqa: F401
+from .attn import decode_attention, hadamard_rotate, kv_decode, kv_encode, kv_encode_rotated  # noqa: F401

@@ -1,5 +1,6 @@
 """Pins for the oracle's KV-cache encoding and decode attention (CPU only)."""
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -80,3 +81,50 @@ def test_attention_large_scores_do_not_overflow_and_pick_the_maximum():
     v = np.array([[[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]]])
     out, _ = oracle.decode_attention(q, k, v, 1.0)
     assert np.all(np.isfinite(out)) and np.allclose(out[0], [1.0, 2.0], rtol=0, atol=1e-40)
+
+
+def _sylvester(d):
+    h = np.array([[1.0]])
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def test_hadamard_rotate_matches_the_matrix_and_is_its_own_inverse():
+    rng = np.random.default_rng(7)
+    for d in (64, 128, 256):
+        # small integers: every sum is exact, so the fast transform equals the matrix product
+        x = rng.integers(-50, 51, size=(3, d)).astype(np.float64)
+        want = x @ _sylvester(d).T * oracle.attn.INV_SQRT[d]
+        assert np.array_equal(oracle.hadamard_rotate(x), want)
+        y = rng.standard_normal((4, d))
+        r = oracle.hadamard_rotate(y)
+        assert np.allclose(np.linalg.norm(r, axis=1), np.linalg.norm(y, axis=1), rtol=1e-14)
+        assert np.allclose(oracle.hadamard_rotate(r), y, rtol=0, atol=1e-13)
+    # a one-hot input gives a constant-magnitude column of H: the rotation spreads an outlier
+    e = np.zeros((1, 256)); e[0, 37] = 1.0
+    assert np.allclose(np.abs(oracle.hadamard_rotate(e)), 1.0 / 16)
+    # each constant is the double nearest 1/sqrt(d): of it and its two neighbours, its square
+    # times d is closest to 1 (exact rational arithmetic)
+    for d, c in oracle.attn.INV_SQRT.items():
+        err = [abs(Fraction(v) ** 2 * d - 1) for v in (math.nextafter(c, 0), c, math.nextafter(c, 1))]
+        assert err[1] < err[0] and err[1] < err[2], d
+
+
+def test_rotated_v_rows_are_bfp4_of_the_rounded_rotation():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((3, 2, 128)).astype(np.float32)
+    exp, code = oracle.kv_encode_rotated(x)
+    assert exp.shape == (2, 3, 8) and code.shape == (2, 3, 64)
+    r = oracle.hadamard_rotate(x).astype(np.float32)
+    e2, c2 = oracle.kv_encode(r, oracle.BFP4)
+    assert np.array_equal(exp, e2) and np.array_equal(code, c2)
+    # attention is linear in v: attention over the rotated values, rotated back, is attention
+    # over the values the rotated cache stands for
+    q = rng.standard_normal((4, 128))
+    k = oracle.kv_decode(*oracle.kv_encode(x), BFP8, 128)
+    vr = oracle.kv_decode(exp, code, oracle.BFP4, 128)
+    out_r, _ = oracle.decode_attention(q, k, vr, 0.1)
+    out, _ = oracle.decode_attention(q, k, oracle.hadamard_rotate(vr), 0.1)
+    assert np.allclose(oracle.hadamard_rotate(out_r), out, rtol=0, atol=1e-12)
+
