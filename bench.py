@@ -345,20 +345,24 @@ def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32", argmax_name=None
 
 
 def attn_workloads(args):
-    """BFP8 KV cache decode attention, 35B-class layer (2 KV heads x 256, 16 query heads), one
-    query token over L cached tokens; bytes = the cache's K and V codes and exponents."""
+    """Decode attention, 35B-class layer (2 KV heads x 256, 16 query heads), one query token
+    over L cached tokens: the BFP8 KV cache, and the long-context cache with BFP8 K and 4-bit V
+    after a Hadamard rotation; bytes = the cache's K and V codes and exponents."""
     import torch
     import block_float_quantized_amd as bfq
     out = {}
     kvh, hd, hq = 2, 256, 16
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
-    for L in (8192, 32768, 131072):
-        per = 2 * kvh * L * (hd + hd // 16)
+    cases = [("BFP8 KV", bfq.KV_V_BFP8, L) for L in (8192, 32768, 131072)]
+    cases += [("BFP8-K 4-bit-V (Hadamard)", bfq.KV_V_BFP4_HADAMARD, L) for L in (32768, 131072, 262144)]
+    for name, vf, L in cases:
+        row = (hd + hd // 16) + ((hd // 2 if vf == bfq.KV_V_BFP4_HADAMARD else hd) + hd // 16)
+        per = kvh * L * row
         R = replicas_for(per, cap=16)
         caches = []
         for r in range(R):
-            c = bfq.KvCache.empty(kvh, hd, L)
+            c = bfq.KvCache.empty(kvh, hd, L, v_format=vf)
             k = torch.randn((L, kvh, hd), device="cuda", generator=gen)
             v = torch.randn((L, kvh, hd), device="cuda", generator=gen)
             bfq.bfp_kv_append(c, k, v, 0)
@@ -369,12 +373,12 @@ def attn_workloads(args):
         ws = workspace(bfq.bfp_attn_decode_workspace_bytes(caches[0], hq, L))
         ms = timed(lambda i: bfq.bfp_attn_decode(caches[i % R], q, L, 1.0 / 16, out=y, workspace=ws),
                    args.steps, args.warmup)
-        out[f"BFP8 KV attention decode L={L}"] = {"us_per_call": round(ms * 1e3, 2),
-                                                  "GB/s": round(per / (ms * 1e-3) / 1e9, 1),
-                                                  "pct_hbm_peak": round(100 * per / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
-                                                  "cache_bytes": per, "replicas": R,
-                                                  "bytes_per_token_layer": 2 * kvh * (hd + hd // 16)}
-        log(f"attention L={L}: {ms * 1e3:.2f} us")
+        out[f"{name} attention decode L={L}"] = {"us_per_call": round(ms * 1e3, 2),
+                                                 "GB/s": round(per / (ms * 1e-3) / 1e9, 1),
+                                                 "pct_hbm_peak": round(100 * per / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                                                 "cache_bytes": per, "replicas": R,
+                                                 "bytes_per_token_layer": kvh * row}
+        log(f"attention {name} L={L}: {ms * 1e3:.2f} us")
         del caches
         torch.cuda.empty_cache()
     return out

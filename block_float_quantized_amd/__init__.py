@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "BFP4", "BFP8", "BfpError", "BfpMatrix", "MoeLayer", "lib", "library_path",
     "bfp_quantize", "bfp_dequantize", "bfp_gemm", "bfp_gemm_workspace_bytes", "bfp_gemm_argmax",
-    "bfp_gemm_argmax_workspace_bytes", "bfp_moe_route", "bfp_moe_dispatch", "KvCache", "bfp_kv_append",
+    "bfp_gemm_argmax_workspace_bytes", "bfp_moe_route", "bfp_moe_dispatch", "KvCache", "KV_V_BFP8", "KV_V_BFP4_HADAMARD", "bfp_kv_append",
     "bfp_attn_decode", "bfp_attn_decode_workspace_bytes",
     "bfp_moe_workspace_bytes", "bfp_moe_forward", "exp_bytes", "code_bytes",
 ]
@@ -63,7 +63,7 @@ class _MoeLayer(ctypes.Structure):
 class _KvCache(ctypes.Structure):
     _fields_ = [("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int64),
                 ("k_exp", ctypes.c_void_p), ("k_code", ctypes.c_void_p), ("v_exp", ctypes.c_void_p),
-                ("v_code", ctypes.c_void_p)]
+                ("v_code", ctypes.c_void_p), ("v_format", ctypes.c_int32)]
 
 
 _LIB = None
@@ -270,9 +270,13 @@ def bfp_gemm_argmax(w: BfpMatrix, x: torch.Tensor, idx: torch.Tensor | None = No
     return idx, val
 
 
+KV_V_BFP8 = 0               # V stored in BFP8 like K
+KV_V_BFP4_HADAMARD = 1      # V rotated by the orthonormal Hadamard transform, stored in BFP4
+
+
 @dataclass
 class KvCache:
-    """A BFP8 KV cache in device memory (see bfp_kv_cache in include/libbfp.h)."""
+    """A BFP KV cache in device memory (see bfp_kv_cache in include/libbfp.h)."""
     kv_heads: int
     head_dim: int
     max_tokens: int
@@ -280,17 +284,19 @@ class KvCache:
     k_code: torch.Tensor
     v_exp: torch.Tensor
     v_code: torch.Tensor
+    v_format: int = KV_V_BFP8
 
     @staticmethod
-    def empty(kv_heads: int, head_dim: int, max_tokens: int, device="cuda") -> "KvCache":
+    def empty(kv_heads: int, head_dim: int, max_tokens: int, device="cuda", v_format: int = KV_V_BFP8) -> "KvCache":
         rows = kv_heads * max_tokens
         ne, nc = exp_bytes(rows, head_dim), code_bytes(BFP8, rows, head_dim)
+        nv = code_bytes(BFP4 if v_format == KV_V_BFP4_HADAMARD else BFP8, rows, head_dim)
         z = lambda n: torch.zeros((n,), dtype=torch.uint8, device=device)
-        return KvCache(kv_heads, head_dim, max_tokens, z(ne), z(nc), z(ne), z(nc))
+        return KvCache(kv_heads, head_dim, max_tokens, z(ne), z(nc), z(ne), z(nv), v_format)
 
     def view(self) -> _KvCache:
         return _KvCache(self.kv_heads, self.head_dim, self.max_tokens, _ptr(self.k_exp), _ptr(self.k_code),
-                        _ptr(self.v_exp), _ptr(self.v_code))
+                        _ptr(self.v_exp), _ptr(self.v_code), self.v_format)
 
     @property
     def nbytes(self) -> int:

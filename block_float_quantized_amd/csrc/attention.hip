@@ -1,10 +1,18 @@
-// BFP8 KV cache for decode attention (gfx950): append (encode) and single-token attention.
+// BFP KV cache for decode attention (gfx950): append (encode) and single-token attention.
 //
 // "Qwen3.6-35B-A3B — TT-native mixed BFP4/BFP8", "Precision as served" (the KV cache is BFP8)
 // and the serving-settings table, KV-precision row: BFP8 halves the cache (20.0 -> 10.6 KiB
 // per token) and, because decode attention reads the whole cache every step, speeds it up at
 // long contexts. Each cached key or value vector (one token, one KV head) is encoded like a
 // weight row: 16-value blocks along head_dim with the weights' exact rounding (bfp_encode.hpp).
+//
+// The long-context cache ("Qwen3.8-27B — TT-native mixed BFP4/BFP8 (GPTQ)", changes in
+// s27-20261005, DFlash2 at 262K) keeps K in BFP8 and stores V in BFP4 after a Hadamard
+// rotation: v -> H v / sqrt(head_dim), H the Sylvester matrix, by the fast transform in fp64
+// (one wave per row, stages of span below the values per lane in registers, the rest across
+// lanes), rounded to fp32 and encoded. Attention then runs over the rotated values; the
+// transform is linear, orthonormal and its own inverse, so each chunk's partial sum is rotated
+// back (in fp32, in LDS) before the merge.
 //
 // Decode attention is split over the sequence (a workgroup per KV head and chunk of tokens):
 //  * the G query heads of a KV head share every key and value row read from HBM;
@@ -27,11 +35,12 @@ namespace {
 
 // One thread per 16-value block of K or V: rows [n][kv_heads][head_dim] -> token slots
 // pos .. pos + n - 1 of every KV head.
+// With v_rot4 only K is encoded here (kv_append_v4r_kernel writes V).
 __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
   const int nb = a.head_dim / kBlock;
   const int64_t per = a.n * a.kv_heads * nb;
   int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= 2 * per) return;
+  if (idx >= (a.v_rot4 ? per : 2 * per)) return;
   const bool is_v = idx >= per;
   if (is_v) idx -= per;
   const int b = (int)(idx % nb);
@@ -62,6 +71,66 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
   uint8_t* exp = (is_v ? a.v_exp : a.k_exp) + row * nb + b;
   uint8_t* code = (is_v ? a.v_code : a.k_code) + (row * nb + b) * kBlock;
   encode_block<8>(u, exp, code);
+}
+
+// The double nearest 1 / sqrt(HD), and its fp32 rounding for the back rotation.
+template <int HD>
+constexpr double kInvSqrtHd = HD == 64 ? 0.125 : HD == 128 ? 0.08838834764831845 : 0.0625;
+
+constexpr int kV4rWaves = 4;
+
+// One wave per V row (token i, KV head g; rows past n idle): H v / sqrt(HD) in fp64, lane l
+// holding elements l P .. l P + P - 1; rounded to fp32, staged in LDS, and encoded in BFP4 by
+// HD / 16 lanes (one block each).
+template <int HD>
+__global__ __launch_bounds__(kV4rWaves * kWave) void kv_append_v4r_kernel(KvAppendArgs a) {
+  constexpr int P = HD / kWave;
+  constexpr int NB = HD / kBlock;
+  __shared__ uint32_t rot[kV4rWaves][HD];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int64_t r = (int64_t)blockIdx.x * kV4rWaves + wave;        // source row i * kv_heads + g
+  const bool valid = r < a.n * a.kv_heads;
+  const int64_t rr = valid ? r : 0;
+  double x[P];
+  if (a.src_bf16) {
+    const uint16_t* src = static_cast<const uint16_t*>(a.v) + rr * HD + lane * P;
+#pragma unroll
+    for (int p = 0; p < P; ++p) x[p] = (double)__uint_as_float((uint32_t)src[p] << 16);
+  } else {
+    const float* src = static_cast<const float*>(a.v) + rr * HD + lane * P;
+#pragma unroll
+    for (int p = 0; p < P; ++p) x[p] = (double)src[p];
+  }
+  // stages of span s: the pair (j, j + s) becomes (x_j + x_j+s, x_j - x_j+s)
+#pragma unroll
+  for (int s = 1; s < P; s <<= 1)
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if ((p & s) == 0) {
+        const double lo = x[p], hi = x[p + s];
+        x[p] = lo + hi;
+        x[p + s] = lo - hi;
+      }
+#pragma unroll
+  for (int s = P; s < HD; s <<= 1) {
+    const int m = s / P;                           // partner lane = lane ^ m
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const double o = __shfl_xor(x[p], m, kWave);
+      x[p] = upper ? o - x[p] : x[p] + o;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p) rot[wave][lane * P + p] = __float_as_uint((float)(x[p] * kInvSqrtHd<HD>));
+  __syncthreads();
+  if (!valid || lane >= NB) return;
+  uint32_t u[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i] = rot[wave][lane * kBlock + i];
+  const int g = (int)(r % a.kv_heads);
+  const int64_t row = (int64_t)g * a.max_tokens + a.pos + r / a.kv_heads;
+  encode_block<4>(u, a.v_exp + row * NB + lane, a.v_code + row * (HD / 2) + lane * 8);
 }
 
 // ---- decode attention ------------------------------------------------------------------
@@ -102,6 +171,21 @@ __device__ __forceinline__ void decode_row8(const Row8& r, float (&w)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) w[i] *= sc;
 }
+// The same for a BFP4 row (4 code bytes per lane; c.y unused).
+template <int HD>
+__device__ __forceinline__ Row8 load_row8_b4(const uint8_t* exp, const uint8_t* code, int64_t row, int sub) {
+  Row8 r;
+  r.c.x = *reinterpret_cast<const uint32_t*>(code + row * (HD / 2) + sub * 4);
+  r.c.y = 0;
+  r.e = exp[row * (HD / kBlock) + sub / 2];
+  return r;
+}
+__device__ __forceinline__ void decode_row8_b4(const Row8& r, float (&w)[8]) {
+  const float sc = block_scale<4>(r.e);
+  unpack8_bfp4(r.c.x, w);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] *= sc;
+}
 
 struct ChunkArgs {
   AttnArgs a;
@@ -110,8 +194,9 @@ struct ChunkArgs {
 };
 
 // Workgroup (c, g): tokens [c chunk, (c + 1) chunk) of KV head g for its G query heads.
-// Writes o_c (unnormalised), m_c and l_c to the workspace.
-template <int HD, int G>
+// Writes o_c (unnormalised), m_c and l_c to the workspace. With V4R the values are the rotated
+// BFP4 ones and o_c is rotated back before it is written.
+template <int HD, int G, bool V4R>
 __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(ChunkArgs ca) {
   constexpr int LPT = HD / 8;                    // lanes per cached row
   constexpr int TPW = kWave / LPT;               // rows per wave step
@@ -206,14 +291,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(ChunkArgs ca) 
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       const int tl = s0 + u * TPS + wave * TPW + grp;
-      r[u] = load_row8<HD>(a.v_exp, a.v_code, row0 + min(tl, nt - 1), sub);
+      if constexpr (V4R) r[u] = load_row8_b4<HD>(a.v_exp, a.v_code, row0 + min(tl, nt - 1), sub);
+      else r[u] = load_row8<HD>(a.v_exp, a.v_code, row0 + min(tl, nt - 1), sub);
     }
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       if (s0 + u * TPS >= ca.chunk) break;
       const int tl = s0 + u * TPS + wave * TPW + grp;
       float vv[8];
-      decode_row8(r[u], vv);
+      if constexpr (V4R) decode_row8_b4(r[u], vv);
+      else decode_row8(r[u], vv);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float p = sc[h][tl];
@@ -236,12 +323,37 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(ChunkArgs ca) 
       for (int i = 0; i < 8; ++i) red[wave][h][sub * 8 + i] = acc[h][i];
   __syncthreads();
   float* po = a.ws + ((int64_t)c * a.q_heads + g * G) * HD;
-  for (int j = threadIdx.x; j < G * HD; j += kAttnThreads) {
-    const int h = j / HD, d = j % HD;
-    float s = red[0][h][d];
+  if constexpr (V4R) {
+    // the sums into sc (no longer read), then H o / sqrt(HD) in place, stage by stage
+    for (int j = threadIdx.x; j < G * HD; j += kAttnThreads) {
+      const int h = j / HD, d = j % HD;
+      float s = red[0][h][d];
 #pragma unroll
-    for (int w = 1; w < kAttnWaves; ++w) s += red[w][h][d];
-    po[(int64_t)h * HD + d] = s;
+      for (int w = 1; w < kAttnWaves; ++w) s += red[w][h][d];
+      sc[h][d] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 1; st < HD; st <<= 1) {
+      for (int j = threadIdx.x; j < G * HD / 2; j += kAttnThreads) {
+        const int h = j / (HD / 2), pi = j % (HD / 2);
+        const int lo = (pi / st) * 2 * st + pi % st;
+        const float x = sc[h][lo], y = sc[h][lo + st];
+        sc[h][lo] = x + y;
+        sc[h][lo + st] = x - y;
+      }
+      __syncthreads();
+    }
+    constexpr float kInv = (float)kInvSqrtHd<HD>;
+    for (int j = threadIdx.x; j < G * HD; j += kAttnThreads) po[j] = sc[j / HD][j % HD] * kInv;
+  } else {
+    for (int j = threadIdx.x; j < G * HD; j += kAttnThreads) {
+      const int h = j / HD, d = j % HD;
+      float s = red[0][h][d];
+#pragma unroll
+      for (int w = 1; w < kAttnWaves; ++w) s += red[w][h][d];
+      po[(int64_t)h * HD + d] = s;
+    }
   }
   if (threadIdx.x < G) {
     float* pml = a.ws + (int64_t)ca.nchunks * a.q_heads * HD + ((int64_t)c * a.q_heads + g * G + threadIdx.x) * 2;
@@ -328,7 +440,10 @@ hipError_t launch_hd_g(const AttnArgs& a, hipStream_t s) {
   ca.a = a;
   ca.chunk = pick_chunk(HD, a.kv_heads, a.L);
   ca.nchunks = (a.L + ca.chunk - 1) / ca.chunk;
-  hipLaunchKernelGGL((attn_chunk_kernel<HD, G>), dim3(ca.nchunks, a.kv_heads), dim3(kAttnThreads), 0, s, ca);
+  if (a.v_rot4)
+    hipLaunchKernelGGL((attn_chunk_kernel<HD, G, true>), dim3(ca.nchunks, a.kv_heads), dim3(kAttnThreads), 0, s, ca);
+  else
+    hipLaunchKernelGGL((attn_chunk_kernel<HD, G, false>), dim3(ca.nchunks, a.kv_heads), dim3(kAttnThreads), 0, s, ca);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(a.q_heads, HD / kMergeDims), dim3(kMergeThreads), 0, s, ca);
@@ -349,9 +464,16 @@ hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t kv_append_launch(const KvAppendArgs& a, hipStream_t s) {
-  const int64_t blocks = 2 * a.n * a.kv_heads * (a.head_dim / kBlock);
+  const int64_t blocks = (a.v_rot4 ? 1 : 2) * a.n * a.kv_heads * (a.head_dim / kBlock);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.v_rot4) return e;
+  const dim3 grid((unsigned)((a.n * a.kv_heads + kV4rWaves - 1) / kV4rWaves));
+  const dim3 block(kV4rWaves * kWave);
+  if (a.head_dim == 64) hipLaunchKernelGGL((kv_append_v4r_kernel<64>), grid, block, 0, s, a);
+  else if (a.head_dim == 128) hipLaunchKernelGGL((kv_append_v4r_kernel<128>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((kv_append_v4r_kernel<256>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// C ABI of the BFP8 KV cache: argument checks for append and decode attention.
+// C ABI of the BFP KV cache (BFP8 K and V, or BFP8 K and rotated BFP4 V): argument checks for append and decode attention.
 #include <hip/hip_runtime.h>
 
 #include "../../include/libbfp.h"
@@ -13,6 +13,7 @@ int32_t check_cache(const bfp_kv_cache* c) {
   if (c->kv_heads < 1 || c->kv_heads > 64 || c->max_tokens < 1 || c->max_tokens > (int64_t)1 << 24) return BFP_E_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return BFP_E_SHAPE;
   if (!c->k_exp || !c->k_code || !c->v_exp || !c->v_code) return BFP_E_ARG;
+  if (c->v_format != BFP_KV_V_BFP8 && c->v_format != BFP_KV_V_BFP4_HADAMARD) return BFP_E_ARG;
   if (!aligned16(c->k_code) || !aligned16(c->v_code)) return BFP_E_ALIGN;
   return BFP_OK;
 }
@@ -36,6 +37,7 @@ int32_t bfp_kv_append(const bfp_kv_cache* c, const void* k, const void* v, int32
   a.n = n; a.pos = pos;
   a.kv_heads = c->kv_heads; a.head_dim = c->head_dim; a.max_tokens = c->max_tokens;
   a.k_exp = c->k_exp; a.k_code = c->k_code; a.v_exp = c->v_exp; a.v_code = c->v_code;
+  a.v_rot4 = c->v_format == BFP_KV_V_BFP4_HADAMARD;
   return from_hip(bfp::kv_append_launch(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -60,6 +62,7 @@ int32_t bfp_attn_decode(const bfp_kv_cache* c, const void* q, int32_t q_dtype, i
   bfp::AttnArgs a{};
   a.k_exp = c->k_exp; a.k_code = c->k_code; a.v_exp = c->v_exp; a.v_code = c->v_code;
   a.kv_heads = c->kv_heads; a.head_dim = c->head_dim; a.max_tokens = c->max_tokens;
+  a.v_rot4 = c->v_format == BFP_KV_V_BFP4_HADAMARD;
   a.q = q; a.q_bf16 = q_dtype == BFP_DT_BF16; a.q_heads = q_heads;
   a.L = (int)seq_len; a.scale = scale; a.out = out; a.ws = static_cast<float*>(ws);
   return from_hip(bfp::attn_decode_launch(a, static_cast<hipStream_t>(stream)));

@@ -14,7 +14,8 @@ struct KvAppendArgs {
   int64_t n, pos;              // rows appended, first token slot
   int kv_heads, head_dim;
   int64_t max_tokens;
-  uint8_t *k_exp, *k_code, *v_exp, *v_code;   // cache planes (BFP8)
+  uint8_t *k_exp, *k_code, *v_exp, *v_code;   // cache planes (K BFP8; V BFP8 or rotated BFP4)
+  int v_rot4;                  // V rotated and stored in BFP4
 };
 hipError_t kv_append_launch(const KvAppendArgs& a, hipStream_t s);
 
@@ -22,6 +23,7 @@ struct AttnArgs {
   const uint8_t *k_exp, *k_code, *v_exp, *v_code;
   int kv_heads, head_dim;
   int64_t max_tokens;
+  int v_rot4;
   const void* q;               // [q_heads][head_dim], fp32 or bf16
   int q_bf16;
   int q_heads;

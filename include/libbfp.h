@@ -251,19 +251,31 @@ int32_t bfp_moe_forward(const bfp_moe_layer *L, const uint16_t *x, int64_t m, fl
  * Layout (device memory owned by the caller), for K and for V alike:
  *   exp  : uint8 [kv_heads][max_tokens][head_dim/16]  (bfp_exp_bytes(kv_heads*max_tokens, head_dim))
  *   code : uint8 [kv_heads][max_tokens][head_dim]     (bfp_code_bytes(BFP_FMT_BFP8, ...))
+ *
+ * v_format BFP_KV_V_BFP4_HADAMARD is the long-context cache of "Qwen3.8-27B — TT-native mixed
+ * BFP4/BFP8 (GPTQ)", changes in s27-20261005 (DFlash2 at 262K): K stays BFP8, V is stored in
+ * 4-bit BFP4 after a Hadamard rotation. Each value vector v is replaced by H v / sqrt(head_dim)
+ * (H the Sylvester Hadamard matrix, H_2n = [[H, H], [H, -H]]), computed in fp64 by the fast
+ * transform (stages of span 1, 2, 4, ...: x_j, x_j+s <- x_j + x_j+s, x_j - x_j+s), times the
+ * double nearest 1/sqrt(head_dim), rounded to fp32, then BFP4-encoded as bfp_quantize does. V
+ * code plane: uint8 [kv_heads][max_tokens][head_dim/2] (value 2j in the low nibble of byte j).
+ * The rotation is orthonormal and its own inverse: bfp_attn_decode rotates its output back.
  */
+#define BFP_KV_V_BFP8 0
+#define BFP_KV_V_BFP4_HADAMARD 1
 typedef struct bfp_kv_cache {
   int32_t kv_heads;       /* 1..64 */
   int32_t head_dim;       /* 64, 128 or 256 */
   int64_t max_tokens;     /* token slots, 1..2^24 */
   uint8_t *k_exp, *k_code, *v_exp, *v_code;
+  int32_t v_format;       /* BFP_KV_V_BFP8 (0) or BFP_KV_V_BFP4_HADAMARD */
 } bfp_kv_cache;
 
 /*
  * Encode n new tokens into slots pos .. pos+n-1 of every KV head. k, v: device
  * [n][kv_heads][head_dim] of dtype (fp32, or bf16 converted exactly). Inputs must be finite
- * (Inf/NaN leave unspecified codes; no synchronisation, unlike bfp_quantize). pos + n must
- * not exceed max_tokens.
+ * (Inf/NaN, or a rotated value beyond the fp32 range, leave unspecified codes; no
+ * synchronisation, unlike bfp_quantize). pos + n must not exceed max_tokens.
  */
 int32_t bfp_kv_append(const bfp_kv_cache *c, const void *k, const void *v, int32_t dtype,
                       int64_t pos, int64_t n, void *stream);
@@ -275,7 +287,8 @@ size_t bfp_attn_decode_workspace_bytes(const bfp_kv_cache *c, int32_t q_heads, i
  * Single-token decode attention over the first seq_len cached tokens, for one sequence:
  *   query head h reads KV head h / (q_heads / kv_heads);
  *   s_t = scale * q[h] . K[t] (decoded keys), p = softmax over t < seq_len,
- *   out[h] = sum_t p_t V[t] (decoded values).
+ *   out[h] = sum_t p_t V[t] (decoded values; with BFP_KV_V_BFP4_HADAMARD the decoded rotated
+ *   values, the sum rotated back by the same transform in fp32).
  * q: device [q_heads][head_dim], fp32 or bf16 (q_dtype); out: device fp32
  * [q_heads][head_dim]. q_heads / kv_heads must be 1, 2, 4 or 8 (else BFP_E_UNSUPPORTED).
  * Products and sums are fp32 (exp via the hardware exp2); the sequence is split into chunks

@@ -110,6 +110,12 @@ def test_kv_cache_host_validation():
     assert lib.bfp_kv_append(ctypes.byref(c), 24, 16, 0, 0, 1, None) == 3                    # misaligned k
     bad = bfq._KvCache(2, 96, 100, 16, 16, 16, 16)
     assert lib.bfp_kv_append(ctypes.byref(bad), 16, 16, 0, 0, 1, None) == 2                   # head_dim
+    fmt = bfq._KvCache(2, 256, 100, 16, 16, 16, 16, 2)
+    assert lib.bfp_kv_append(ctypes.byref(fmt), 16, 16, 0, 0, 1, None) == 1                   # v_format
+    assert lib.bfp_attn_decode_workspace_bytes(ctypes.byref(fmt), 16, 100) == 0
+    rot = bfq._KvCache(2, 256, 100, 16, 16, 16, 16, bfq.KV_V_BFP4_HADAMARD)
+    assert lib.bfp_attn_decode_workspace_bytes(ctypes.byref(rot), 16, 100) > 0
+    assert lib.bfp_kv_append(ctypes.byref(rot), 16, 16, 0, 90, 11, None) == 2
     need = lib.bfp_attn_decode_workspace_bytes(ctypes.byref(c), 16, 100)
     assert need > 0 and lib.bfp_attn_decode_workspace_bytes(ctypes.byref(c), 16, 101) == 0
     assert lib.bfp_attn_decode(ctypes.byref(c), 16, 0, 16, 0, 1.0, 16, 16, need, None) == 2   # seq_len 0

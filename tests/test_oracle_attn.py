@@ -128,3 +128,18 @@ def test_rotated_v_rows_are_bfp4_of_the_rounded_rotation():
     out, _ = oracle.decode_attention(q, k, oracle.hadamard_rotate(vr), 0.1)
     assert np.allclose(oracle.hadamard_rotate(out_r), out, rtol=0, atol=1e-12)
 
+
+
+def test_rotated_cache_bytes_per_token_match_the_card():
+    """The 27B card ("Qwen3.8-27B — TT-native mixed BFP4/BFP8 (GPTQ)", changes in s27-20261005,
+    DFlash2 at 262K) gives 26,624 bytes per token for the BFP8-K / 4-bit-V cache against 34,816
+    for the BFP8 KV cache. Both follow from the 16-value block layout with one exponent byte per
+    block, for a model whose cached head dimensions add up to 16,384 per token: BFP8 rows cost
+    17/16 bytes per value, BFP4 rows 9/16."""
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((1, 64, 256)).astype(np.float32)          # one token, 64 x 256 = 16,384
+    ek, ck = oracle.kv_encode(x)
+    ev, cv = oracle.kv_encode_rotated(x)
+    assert ek.nbytes + ck.nbytes + ev.nbytes + cv.nbytes == 26624
+    ev8, cv8 = oracle.kv_encode(x)
+    assert ek.nbytes + ck.nbytes + ev8.nbytes + cv8.nbytes == 34816
