@@ -31,6 +31,8 @@ namespace bfp {
 
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
 // ---- append ----------------------------------------------------------------------------
 
 // One thread per 16-value block of K or V: rows [n][kv_heads][head_dim] -> token slots
@@ -362,62 +364,335 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(ChunkArgs ca) 
   }
 }
 
-// Workgroup (h, j): dimensions [64 j, 64 j + 64) of query head h, merged over the chunks. The
-// maximum M of the chunk maxima first; then kMergeGroups thread groups (one thread per
-// dimension) each add a fixed residue class of chunks in chunk order, eight chunks' loads in
-// flight per thread, and the groups' sums are added in group order: the result does not
-// depend on scheduling.
+// Matrix-core variant for G = 8 query heads per KV head, on the fp32 matrix instruction
+// (v_mfma_f32_16x16x4f32: D[16x16] += A[16x4] B[4x16]; lane l supplies A[l%16][l/16] and
+// B[l/16][l%16] and holds D[4 (l/16) + i][l%16], i < 4). Inputs stay fp32 as in the ALU kernel.
+// Each wave takes tiles of 16 tokens (tiles wave, wave + 4, ... of the chunk):
+//  * scores S^T = K Q^T: lane (j = l/16, r = l%16) supplies token r's dimensions
+//    [HD/4 j, HD/4 (j+1)) one per step (a contiguous HD/4-byte piece of its row) as A, and the
+//    same dimensions of query head r (zero for r >= 8) as B; D gives lane (j, r) the scores of
+//    tokens 4 j + i for head r;
+//  * the chunk's maximum per head (over lanes, then waves through LDS), p = exp(s - m) in place;
+//  * O = P V: step u takes the tokens 4 j + u of a tile, so lane (j, r) supplies its own p of
+//    register u as A, and as B the dimensions [HD/16 r, HD/16 (r+1)) of that token's value
+//    row (one whole 16-value block at HD = 256), one output tile per dimension of the piece.
+// The partial sums of the waves are added in wave order, as in the ALU kernel.
+constexpr int kMfmaTile = 16;
+#ifndef ATTN_PREFETCH
+#define ATTN_PREFETCH 1
+#endif
+constexpr int kPrefetch = ATTN_PREFETCH;         // tiles whose rows are in flight ahead of use
+
+// Raw cached rows of one lane: a tile's key piece, a value piece (codes and exponent bytes).
+template <int HD>
+struct KPiece {
+  uint4 c[HD / 64];
+  uint32_t e;
+};
+struct VPiece {
+  uint4 c;
+  uint32_t e;
+};
+
+// NT: tiles per wave (the chunk is 64 NT tokens).
+template <int HD, bool V4R, int NT>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkArgs ca) {
+  constexpr int G = 8;
+  constexpr int QK = HD / 4;                     // score steps; dims per lane group
+  constexpr int DPC = HD / 16;                   // value dims per lane column = output tiles
+  constexpr int QS = HD + 8;                     // LDS row stride of the query parts (conflict-free b128 reads)
+  __shared__ float red[kAttnWaves][G][HD];
+  __shared__ __align__(16) uint16_t qs[3][16][QS];
+  __shared__ float wstat[kAttnWaves][16], wsum[kAttnWaves][16], wfac[kAttnWaves][G];
+  __shared__ float mrow[G], lrow[G];
+  const AttnArgs& a = ca.a;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int j = lane >> 4, r = lane & 15;
+  const int c = blockIdx.x, g = blockIdx.y;
+  const int t0 = c * ca.chunk;
+  const int nt = min(ca.chunk, a.L - t0);
+  const int64_t row0 = (int64_t)g * a.max_tokens + t0;
+
+  auto kload = [&](int tile, KPiece<HD>& k) {
+    const int64_t row = row0 + min(tile * kMfmaTile + r, nt - 1);
+    const uint4* pc = reinterpret_cast<const uint4*>(a.k_code + row * HD + QK * j);
+#pragma unroll
+    for (int v = 0; v < HD / 64; ++v) k.c[v] = pc[v];
+    const uint8_t* pe = a.k_exp + row * (HD / kBlock) + (QK / 16) * j;
+    if constexpr (HD == 256) k.e = *reinterpret_cast<const uint32_t*>(pe);
+    else if constexpr (HD == 128) k.e = *reinterpret_cast<const uint16_t*>(pe);
+    else k.e = *pe;
+  };
+  // value piece of token tile * 16 + 4 j + u: dims [DPC r, DPC r + DPC)
+  auto vload = [&](int tile, int u, VPiece& v) {
+    const int64_t row = row0 + min(tile * kMfmaTile + 4 * j + u, nt - 1);
+    v.e = a.v_exp[row * (HD / kBlock) + (DPC * r) / kBlock];
+    constexpr int bytes = V4R ? DPC / 2 : DPC;
+    const uint8_t* pc = a.v_code + row * (V4R ? HD / 2 : HD) + bytes * r;
+    v.c = uint4{0u, 0u, 0u, 0u};
+    if constexpr (bytes == 16) v.c = *reinterpret_cast<const uint4*>(pc);
+    else if constexpr (bytes == 8) { const uint2 x = *reinterpret_cast<const uint2*>(pc); v.c.x = x.x; v.c.y = x.y; }
+    else if constexpr (bytes == 4) v.c.x = *reinterpret_cast<const uint32_t*>(pc);
+    else v.c.x = *reinterpret_cast<const uint16_t*>(pc);
+  };
+
+  // queries times the scale in LDS as three bf16 parts (hi + mid + lo, about 24 significant
+  // bits together), rows 8..15 zero
+  for (int x = threadIdx.x; x < 16 * HD; x += kAttnThreads) {
+    const int h = x / HD, d = x % HD;
+    float q = 0.f;
+    if (h < G) {
+      const int64_t o = (int64_t)(g * G + h) * HD + d;
+      q = (a.q_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.q)[o] << 16)
+                    : static_cast<const float*>(a.q)[o]) * a.scale;
+    }
+    const uint32_t hi = f32_to_bf16_rne(q);
+    const float r1 = q - __uint_as_float(hi << 16);
+    const uint32_t mid = f32_to_bf16_rne(r1);
+    const uint32_t lo = f32_to_bf16_rne(r1 - __uint_as_float(mid << 16));
+    qs[0][h][d] = (uint16_t)hi;
+    qs[1][h][d] = (uint16_t)mid;
+    qs[2][h][d] = (uint16_t)lo;
+  }
+
+  // one pass over the wave's tiles with a running maximum m (head r) and, per lane, a running
+  // sum l of its own probabilities; the keys and values of the tile kPrefetch ahead load during
+  // this tile
+  KPiece<HD> kb[NT];
+  VPiece vb[NT][4];
+  // (no load sits in a branch: a branch lets the compiler place the use of the result, and so a
+  // wait for it, right after the load)
+  auto load_tile = [&](int tt) {
+    const int tile = wave + tt * kAttnWaves;
+    kload(tile, kb[tt]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vload(tile, u, vb[tt][u]);
+  };
+#pragma unroll
+  for (int p = 0; p < kPrefetch; ++p) load_tile(p);
+  __syncthreads();                               // queries in LDS
+
+  float m = -__builtin_inff(), l = 0.f;
+  f32x4 O[DPC];
+#pragma unroll
+  for (int n = 0; n < DPC; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int tile = wave + tt * kAttnWaves;
+    if (tt + kPrefetch < NT) load_tile(tt + kPrefetch);
+    const KPiece<HD>& kc = kb[tt];
+    const VPiece (&vc)[4] = vb[tt];
+    // scores of tokens 4 j + i, head r
+    const uint32_t* code = reinterpret_cast<const uint32_t*>(kc.c);
+    // bf16 products (v_mfma_f32_16x16x32_bf16, A = 8 key values of lane group j, B = the
+    // same dims of query head r): the keys are exact in bf16 (at most 8 significant bits, the
+    // block scale a power of two), the query is the sum of its three parts; per part an
+    // accumulator of its own, added at the end
+    f32x4 acc[3];
+#pragma unroll
+    for (int e = 0; e < 3; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < QK / 8; ++st) {
+      const float scl = block_scale<8>((kc.e >> (8 * (st / 2))) & 0xffu);
+      float kv[8];
+      unpack4_bfp8(code[2 * st], kv);
+      unpack4_bfp8(code[2 * st + 1], kv + 4);
+      uint32_t kp2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        kp2[e] = __builtin_amdgcn_perm(__float_as_uint(kv[2 * e + 1] * scl), __float_as_uint(kv[2 * e] * scl),
+                                       0x07060302u);
+      const bf16x8 kb = __builtin_bit_cast(bf16x8, kp2);
+#pragma unroll
+      for (int e = 0; e < 3; ++e) {
+        const bf16x8 qb = *reinterpret_cast<const bf16x8*>(&qs[e][r][QK * j + 8 * st]);
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, acc[e], 0, 0, 0);
+      }
+    }
+    const f32x4 as = acc[0] + (acc[1] + acc[2]);
+    float S[4] = {as.x, as.y, as.z, as.w};
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      S[i] = (r < G && tile * kMfmaTile + 4 * j + i < nt) ? S[i] : -__builtin_inff();
+      tmax = fmaxf(tmax, S[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float mn = fmaxf(m, tmax);
+    const float alpha = mn == -__builtin_inff() ? 1.f : __expf(m - mn);
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      S[i] = S[i] == -__builtin_inff() ? 0.f : __expf(S[i] - mn);
+      l += S[i];
+    }
+    // O rows are heads 4 j + i: their factors come from lanes r = 4 j + i (skipped when no
+    // head's maximum moved)
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = __shfl(alpha, (4 * j + i) & 15, kWave);
+#pragma unroll
+        for (int n = 0; n < DPC; ++n) O[n][i] *= f;
+      }
+    }
+    // O += P V
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float vv[DPC];
+      const uint32_t cw[4] = {vc[u].c.x, vc[u].c.y, vc[u].c.z, vc[u].c.w};
+      if constexpr (V4R) {
+        const float sc = block_scale<4>(vc[u].e);
+        if constexpr (DPC >= 8) {
+#pragma unroll
+          for (int b = 0; b < DPC / 8; ++b) unpack8_bfp4(cw[b], vv + 8 * b);
+        } else {
+          float t8[8];
+          unpack8_bfp4(cw[0], t8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = t8[e];
+        }
+#pragma unroll
+        for (int e = 0; e < DPC; ++e) vv[e] *= sc;
+      } else {
+        const float sc = block_scale<8>(vc[u].e);
+#pragma unroll
+        for (int b = 0; b < DPC / 4; ++b) unpack4_bfp8(cw[b], vv + 4 * b);
+#pragma unroll
+        for (int e = 0; e < DPC; ++e) vv[e] *= sc;
+      }
+#pragma unroll
+      for (int n = 0; n < DPC; ++n) O[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(S[u], vv[n], O[n], 0, 0, 0);
+    }
+  }
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+
+  // the waves' (m, l, O) combined in wave order: M = max m_w, O = sum_w e^(m_w - M) O_w
+  if (j == 0) {
+    wstat[wave][r] = m;
+    wsum[wave][r] = l;
+  }
+  if (j < 2)
+#pragma unroll
+    for (int n = 0; n < DPC; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][4 * j + i][DPC * r + n] = O[n][i];
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float M = wstat[0][h];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, wstat[w][h]);
+    float ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float f = wstat[w][h] == -__builtin_inff() ? 0.f : __expf(wstat[w][h] - M);
+      wfac[w][h] = f;
+      ls += f * wsum[w][h];
+    }
+    mrow[h] = M;
+    lrow[h] = ls;
+  }
+  __syncthreads();
+  float* po = a.ws + ((int64_t)c * a.q_heads + g * G) * HD;
+  if constexpr (V4R) {
+    for (int x = threadIdx.x; x < G * HD; x += kAttnThreads) {
+      const int h = x / HD, d = x % HD;
+      float s2 = wfac[0][h] * red[0][h][d];
+#pragma unroll
+      for (int w = 1; w < kAttnWaves; ++w) s2 = __builtin_fmaf(wfac[w][h], red[w][h][d], s2);
+      red[0][h][d] = s2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 1; st < HD; st <<= 1) {
+      for (int x = threadIdx.x; x < G * HD / 2; x += kAttnThreads) {
+        const int h = x / (HD / 2), pi = x % (HD / 2);
+        const int lo = (pi / st) * 2 * st + pi % st;
+        const float y0 = red[0][h][lo], y1 = red[0][h][lo + st];
+        red[0][h][lo] = y0 + y1;
+        red[0][h][lo + st] = y0 - y1;
+      }
+      __syncthreads();
+    }
+    constexpr float kInv = (float)kInvSqrtHd<HD>;
+    for (int x = threadIdx.x; x < G * HD; x += kAttnThreads) po[x] = red[0][x / HD][x % HD] * kInv;
+  } else {
+    for (int x = threadIdx.x; x < G * HD; x += kAttnThreads) {
+      const int h = x / HD, d = x % HD;
+      float s2 = wfac[0][h] * red[0][h][d];
+#pragma unroll
+      for (int w = 1; w < kAttnWaves; ++w) s2 = __builtin_fmaf(wfac[w][h], red[w][h][d], s2);
+      po[(int64_t)h * HD + d] = s2;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float* pml = a.ws + (int64_t)ca.nchunks * a.q_heads * HD + ((int64_t)c * a.q_heads + g * G + threadIdx.x) * 2;
+    pml[0] = mrow[threadIdx.x];
+    pml[1] = lrow[threadIdx.x];
+  }
+}
+
+// Workgroup (h, j): dimensions [64 j, 64 j + 64) of query head h, merged over the chunks.
+// kMergeGroups thread groups of 16 threads (four dimensions each, one 16-byte load per chunk)
+// each fold a fixed residue class of chunks in chunk order into a running (m, l, o) (eight
+// chunks' loads in flight per thread); the groups' results are then combined in group order,
+// so the result does not depend on scheduling.
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeDims = 64;
-constexpr int kMergeGroups = kMergeThreads / kMergeDims;
+constexpr int kMergeTpr = kMergeDims / 4;                 // threads per chunk row
+constexpr int kMergeGroups = kMergeThreads / kMergeTpr;
 template <int HD>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(ChunkArgs ca) {
-  constexpr int GT = kMergeDims;                     // threads per group
   constexpr int U = 8;
-  __shared__ float wmax[kMergeThreads / kWave];
-  __shared__ float po[kMergeGroups][GT], pl[kMergeGroups];
+  __shared__ float gm[kMergeGroups], gl[kMergeGroups];
+  __shared__ __align__(16) float go[kMergeGroups][kMergeDims];
   const AttnArgs& a = ca.a;
   const int h = blockIdx.x, tid = threadIdx.x;
   const int d0 = blockIdx.y * kMergeDims;
+  const int grp = tid / kMergeTpr, qd = 4 * (tid % kMergeTpr);
   const float* ml = a.ws + (int64_t)ca.nchunks * a.q_heads * HD;
-  float mx = -__builtin_inff();
-  for (int c = tid; c < ca.nchunks; c += kMergeThreads) mx = fmaxf(mx, ml[((int64_t)c * a.q_heads + h) * 2]);
-  mx = wave_max(mx);
-  if ((tid & (kWave - 1)) == 0) wmax[tid / kWave] = mx;
-  __syncthreads();
-  mx = wmax[0];
+  float m = -__builtin_inff(), l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = grp; c0 < ca.nchunks; c0 += kMergeGroups * U) {
+    float mc[U], lc[U];
+    f32x4 oc[U];
 #pragma unroll
-  for (int w = 1; w < kMergeThreads / kWave; ++w) mx = fmaxf(mx, wmax[w]);
-  const int grp = tid / GT, d = d0 + tid % GT;
-  float l = 0.f, o = 0.f;
-  {
-    for (int c0 = grp; c0 < ca.nchunks; c0 += kMergeGroups * U) {
-      float m[U], lv[U], ov[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = min(c0 + u * kMergeGroups, ca.nchunks - 1);
-        m[u] = ml[((int64_t)c * a.q_heads + h) * 2];
-        lv[u] = ml[((int64_t)c * a.q_heads + h) * 2 + 1];
-        ov[u] = a.ws[((int64_t)c * a.q_heads + h) * HD + d];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (c0 + u * kMergeGroups >= ca.nchunks) break;
-        const float w = __expf(m[u] - mx);
-        l = __builtin_fmaf(w, lv[u], l);
-        o = __builtin_fmaf(w, ov[u], o);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int c = min(c0 + u * kMergeGroups, ca.nchunks - 1);
+      const int64_t row = (int64_t)c * a.q_heads + h;
+      mc[u] = ml[row * 2];
+      lc[u] = ml[row * 2 + 1];
+      oc[u] = *reinterpret_cast<const f32x4*>(a.ws + row * HD + d0 + qd);
     }
-    po[grp][tid % GT] = o;
-    if (tid % GT == 0) pl[grp] = l;
-  }
-  __syncthreads();
-  if (tid < GT) {
-    float os = po[0][tid], ls = pl[0];
 #pragma unroll
-    for (int j = 1; j < kMergeGroups; ++j) {
-      os += po[j][tid];
-      ls += pl[j];
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u * kMergeGroups >= ca.nchunks) break;
+      const float mn = fmaxf(m, mc[u]);              // every chunk's maximum is finite
+      const float fa = __expf(m - mn), fb = __expf(mc[u] - mn);
+      l = l * fa + lc[u] * fb;
+      o = o * fa + oc[u] * fb;
+      m = mn;
+    }
+  }
+  if (tid % kMergeTpr == 0) {
+    gm[grp] = m;
+    gl[grp] = l;
+  }
+  *reinterpret_cast<f32x4*>(&go[grp][qd]) = o;
+  __syncthreads();
+  if (tid < kMergeDims) {
+    float M = gm[0];
+    for (int g = 1; g < kMergeGroups; ++g) M = fmaxf(M, gm[g]);
+    float os = 0.f, ls = 0.f;
+    for (int g = 0; g < kMergeGroups; ++g) {
+      const float f = gm[g] == -__builtin_inff() ? 0.f : __expf(gm[g] - M);
+      os = __builtin_fmaf(f, go[g][tid], os);
+      ls = __builtin_fmaf(f, gl[g], ls);
     }
     a.out[(int64_t)h * HD + d0 + tid] = os / ls;
   }
@@ -426,12 +701,19 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(ChunkArgs ca)
 template <int HD>
 constexpr int tokens_per_step() { return kAttnWaves * (kWave / (HD / 8)); }
 
-// Tokens per workgroup: about 256 workgroups in all, between 64 and kMaxChunk tokens.
+// Tokens per workgroup: about 256 workgroups in all, a multiple of 64 between 64 and kMaxChunk
+// (a whole number of steps of either kernel).
 inline int pick_chunk(int head_dim, int kv_heads, int L) {
-  const int tps = kAttnWaves * (kWave / (head_dim / 8));
+  (void)head_dim;
   int ch = (int)(((int64_t)L * kv_heads + 255) / 256);
   ch = ch < 64 ? 64 : ch > kMaxChunk ? kMaxChunk : ch;
-  return (ch + tps - 1) / tps * tps;
+  return (ch + 63) / 64 * 64;
+}
+
+template <int HD, int NT>
+void launch_mfma(const ChunkArgs& ca, dim3 grid, hipStream_t s) {
+  if (ca.a.v_rot4) hipLaunchKernelGGL((attn_chunk_mfma_kernel<HD, true, NT>), grid, dim3(kAttnThreads), 0, s, ca);
+  else hipLaunchKernelGGL((attn_chunk_mfma_kernel<HD, false, NT>), grid, dim3(kAttnThreads), 0, s, ca);
 }
 
 template <int HD, int G>
@@ -440,10 +722,18 @@ hipError_t launch_hd_g(const AttnArgs& a, hipStream_t s) {
   ca.a = a;
   ca.chunk = pick_chunk(HD, a.kv_heads, a.L);
   ca.nchunks = (a.L + ca.chunk - 1) / ca.chunk;
-  if (a.v_rot4)
-    hipLaunchKernelGGL((attn_chunk_kernel<HD, G, true>), dim3(ca.nchunks, a.kv_heads), dim3(kAttnThreads), 0, s, ca);
-  else
-    hipLaunchKernelGGL((attn_chunk_kernel<HD, G, false>), dim3(ca.nchunks, a.kv_heads), dim3(kAttnThreads), 0, s, ca);
+  const dim3 grid(ca.nchunks, a.kv_heads);
+  if constexpr (G == 8) {
+    switch (ca.chunk / (kAttnWaves * kMfmaTile)) {
+      case 1: launch_mfma<HD, 1>(ca, grid, s); break;
+      case 2: launch_mfma<HD, 2>(ca, grid, s); break;
+      case 3: launch_mfma<HD, 3>(ca, grid, s); break;
+      default: launch_mfma<HD, 4>(ca, grid, s); break;
+    }
+  } else {
+    if (a.v_rot4) hipLaunchKernelGGL((attn_chunk_kernel<HD, G, true>), grid, dim3(kAttnThreads), 0, s, ca);
+    else hipLaunchKernelGGL((attn_chunk_kernel<HD, G, false>), grid, dim3(kAttnThreads), 0, s, ca);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(a.q_heads, HD / kMergeDims), dim3(kMergeThreads), 0, s, ca);

@@ -83,7 +83,9 @@ def test_kv_append_bit_exact(dtype):
         assert all(not r.any() for r in rest), "slots past the appended tokens were written"
 
 
+# group 8 runs on the matrix cores, smaller groups on the vector ALUs
 @pytest.mark.parametrize("kvh,group,hd,L", [(2, 8, 256, 1), (2, 8, 256, 5), (2, 8, 256, 257), (2, 8, 256, 3000),
+                                            (1, 8, 64, 300), (3, 8, 128, 777), (1, 8, 64, 70000),
                                             (1, 1, 64, 100), (4, 2, 128, 1000), (2, 4, 256, 10000),
                                             (8, 1, 128, 64)])
 @pytest.mark.parametrize("qdt", ["f32", "bf16"])
@@ -195,6 +197,7 @@ def test_kv_append_v4r_outliers_and_tiny_values():
 
 
 @pytest.mark.parametrize("kvh,group,hd,L", [(2, 8, 256, 1), (2, 8, 256, 257), (2, 8, 256, 3000),
+                                            (1, 8, 64, 300), (3, 8, 128, 777),
                                             (1, 1, 64, 100), (4, 2, 128, 1000), (2, 4, 256, 10000),
                                             (8, 1, 128, 64)])
 @pytest.mark.parametrize("qdt", ["f32", "bf16"])
