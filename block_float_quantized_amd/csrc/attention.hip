@@ -32,6 +32,7 @@ namespace bfp {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // ---- append ----------------------------------------------------------------------------
 
@@ -538,33 +539,52 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
         for (int n = 0; n < DPC; ++n) O[n][i] *= f;
       }
     }
-    // O += P V
+    // O += P V on v_mfma_f32_16x16x16_bf16 over the tile's 16 tokens: lane (j, r) supplies as
+    // A its own probabilities (tokens 4 j + i, head r) as hi + lo bf16 parts, and as B the
+    // value dims DPC r + n of those four tokens (exact in bf16), one product per n
+    uint32_t ph[2], pl[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t h0 = __float_as_uint(S[2 * e]) & 0xffff0000u, h1 = __float_as_uint(S[2 * e + 1]) & 0xffff0000u;
+      ph[e] = h1 | (h0 >> 16);
+      const uint32_t l0 = f32_to_bf16_rne(S[2 * e] - __uint_as_float(h0));
+      const uint32_t l1 = f32_to_bf16_rne(S[2 * e + 1] - __uint_as_float(h1));
+      pl[e] = (l1 << 16) | l0;
+    }
+    const s16x4 pah = __builtin_bit_cast(s16x4, ph), pal = __builtin_bit_cast(s16x4, pl);
+    float vv[4][DPC];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      float vv[DPC];
       const uint32_t cw[4] = {vc[u].c.x, vc[u].c.y, vc[u].c.z, vc[u].c.w};
       if constexpr (V4R) {
         const float sc = block_scale<4>(vc[u].e);
         if constexpr (DPC >= 8) {
 #pragma unroll
-          for (int b = 0; b < DPC / 8; ++b) unpack8_bfp4(cw[b], vv + 8 * b);
+          for (int b = 0; b < DPC / 8; ++b) unpack8_bfp4(cw[b], vv[u] + 8 * b);
         } else {
           float t8[8];
           unpack8_bfp4(cw[0], t8);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vv[e] = t8[e];
+          for (int e = 0; e < 4; ++e) vv[u][e] = t8[e];
         }
 #pragma unroll
-        for (int e = 0; e < DPC; ++e) vv[e] *= sc;
+        for (int e = 0; e < DPC; ++e) vv[u][e] *= sc;
       } else {
         const float sc = block_scale<8>(vc[u].e);
 #pragma unroll
-        for (int b = 0; b < DPC / 4; ++b) unpack4_bfp8(cw[b], vv + 4 * b);
+        for (int b = 0; b < DPC / 4; ++b) unpack4_bfp8(cw[b], vv[u] + 4 * b);
 #pragma unroll
-        for (int e = 0; e < DPC; ++e) vv[e] *= sc;
+        for (int e = 0; e < DPC; ++e) vv[u][e] *= sc;
       }
+    }
 #pragma unroll
-      for (int n = 0; n < DPC; ++n) O[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(S[u], vv[n], O[n], 0, 0, 0);
+    for (int n = 0; n < DPC; ++n) {
+      uint32_t vb[2];
+      vb[0] = __builtin_amdgcn_perm(__float_as_uint(vv[1][n]), __float_as_uint(vv[0][n]), 0x07060302u);
+      vb[1] = __builtin_amdgcn_perm(__float_as_uint(vv[3][n]), __float_as_uint(vv[2][n]), 0x07060302u);
+      const s16x4 bv = __builtin_bit_cast(s16x4, vb);
+      O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pah, bv, O[n], 0, 0, 0);
+      O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pal, bv, O[n], 0, 0, 0);
     }
   }
   l += __shfl_xor(l, 16, kWave);
