@@ -34,6 +34,28 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// Magnitudes of the four BFP8 codes of c as fp32 (v_cvt_f32_ubyte0..3 of the masked word; the
+// mask is opaque to the compiler so that it keeps the byte conversions).
+__device__ __forceinline__ void mag4_bfp8(uint32_t c, float m[4]) {
+  uint32_t t;
+  asm("v_and_b32 %0, 0x7f7f7f7f, %1" : "=v"(t) : "v"(c));
+  m[0] = (float)(t & 0xffu);
+  m[1] = (float)((t >> 8) & 0xffu);
+  m[2] = (float)((t >> 16) & 0xffu);
+  m[3] = (float)(t >> 24);
+}
+// bf16 pair (lo = a, hi = b) of two fp32 values exact in bf16, with the sign bits of code bytes
+// sa of ca and sb of cb (byte selectors of v_perm: sa in 0..3 of ca, sb in 4..7 of cb).
+__device__ __forceinline__ uint32_t signed_pair(float a, float b, uint32_t ca, uint32_t cb, uint32_t sel) {
+  const uint32_t p = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+  return p ^ (__builtin_amdgcn_perm(cb, ca, sel) & 0x80008000u);
+}
+// selector placing byte ka of the low source at byte 1 and byte kb (4..7: of the high source)
+// at byte 3, zeros elsewhere
+__device__ __forceinline__ constexpr uint32_t sign_sel(int ka, int kb) {
+  return ((uint32_t)kb << 24) | (0x0cu << 16) | ((uint32_t)ka << 8) | 0x0cu;
+}
+
 // ---- append ----------------------------------------------------------------------------
 
 // One thread per 16-value block of K or V: rows [n][kv_heads][head_dim] -> token slots
@@ -495,14 +517,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
 #pragma unroll
     for (int st = 0; st < QK / 8; ++st) {
       const float scl = block_scale<8>((kc.e >> (8 * (st / 2))) & 0xffu);
+      const uint32_t c0 = code[2 * st], c1 = code[2 * st + 1];
       float kv[8];
-      unpack4_bfp8(code[2 * st], kv);
-      unpack4_bfp8(code[2 * st + 1], kv + 4);
-      uint32_t kp2[4];
+      mag4_bfp8(c0, kv);
+      mag4_bfp8(c1, kv + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        kp2[e] = __builtin_amdgcn_perm(__float_as_uint(kv[2 * e + 1] * scl), __float_as_uint(kv[2 * e] * scl),
-                                       0x07060302u);
+      for (int e = 0; e < 8; ++e) kv[e] *= scl;
+      uint32_t kp2[4];
+      kp2[0] = signed_pair(kv[0], kv[1], c0, c0, sign_sel(0, 5));
+      kp2[1] = signed_pair(kv[2], kv[3], c0, c0, sign_sel(2, 7));
+      kp2[2] = signed_pair(kv[4], kv[5], c1, c1, sign_sel(0, 5));
+      kp2[3] = signed_pair(kv[6], kv[7], c1, c1, sign_sel(2, 7));
       const bf16x8 kb = __builtin_bit_cast(bf16x8, kp2);
 #pragma unroll
       for (int e = 0; e < 3; ++e) {
@@ -572,7 +597,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
       } else {
         const float sc = block_scale<8>(vc[u].e);
 #pragma unroll
-        for (int b = 0; b < DPC / 4; ++b) unpack4_bfp8(cw[b], vv[u] + 4 * b);
+        for (int b = 0; b < DPC / 4; ++b) mag4_bfp8(cw[b], vv[u] + 4 * b);   // signs added below
 #pragma unroll
         for (int e = 0; e < DPC; ++e) vv[u][e] *= sc;
       }
@@ -580,8 +605,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
 #pragma unroll
     for (int n = 0; n < DPC; ++n) {
       uint32_t vb[2];
-      vb[0] = __builtin_amdgcn_perm(__float_as_uint(vv[1][n]), __float_as_uint(vv[0][n]), 0x07060302u);
-      vb[1] = __builtin_amdgcn_perm(__float_as_uint(vv[3][n]), __float_as_uint(vv[2][n]), 0x07060302u);
+      if constexpr (V4R) {
+        vb[0] = __builtin_amdgcn_perm(__float_as_uint(vv[1][n]), __float_as_uint(vv[0][n]), 0x07060302u);
+        vb[1] = __builtin_amdgcn_perm(__float_as_uint(vv[3][n]), __float_as_uint(vv[2][n]), 0x07060302u);
+      } else {
+        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vc[0].c);
+        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vc[1].c);
+        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vc[2].c);
+        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vc[3].c);
+        const uint32_t sel = sign_sel(n % 4, 4 + n % 4);
+        vb[0] = signed_pair(vv[0][n], vv[1][n], w0[n / 4], w1[n / 4], sel);
+        vb[1] = signed_pair(vv[2][n], vv[3][n], w2[n / 4], w3[n / 4], sel);
+      }
       const s16x4 bv = __builtin_bit_cast(s16x4, vb);
       O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pah, bv, O[n], 0, 0, 0);
       O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pal, bv, O[n], 0, 0, 0);
