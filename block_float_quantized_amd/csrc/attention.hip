@@ -14,15 +14,14 @@
 // transform is linear, orthonormal and its own inverse, so each chunk's partial sum is rotated
 // back (in fp32, in LDS) before the merge.
 //
-// Decode attention is split over the sequence (a workgroup per KV head and chunk of tokens):
-//  * the G query heads of a KV head share every key and value row read from HBM;
-//  * head_dim / 8 lanes hold one cached row, 8 values each (one 8-byte code load and one
-//    exponent byte per lane: a wave load covers whole consecutive rows);
-//  * scores: 8 products per query head per lane, then a lane-group reduction that leaves one
-//    head's score per writer lane (stored in LDS with the chunk's other scores);
-//  * per head the chunk's maximum m and sum l of exp(s - m), then sum_t exp(s_t - m) v_t;
-//  * attn_merge_kernel combines the chunks in chunk order: out = sum_c e^(m_c - M) o_c /
-//    sum_c e^(m_c - M) l_c. Every order is fixed, so results do not depend on scheduling.
+// Decode attention is split over the sequence (a workgroup per KV head and chunk of tokens); the
+// G query heads of a KV head share every key and value row read from HBM. Each chunk yields
+// its maximum m_c, sum l_c of exp(s - m_c) and unnormalised o_c = sum_t exp(s_t - m_c) v_t;
+// attn_merge_kernel combines them, out = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
+// Every order is fixed, so results do not depend on scheduling. Two chunk kernels:
+//  * G = 8 (attn_chunk_mfma_kernel): both products on the bf16 matrix instructions;
+//  * G = 1, 2, 4 (attn_chunk_kernel): fp32 FMAs, head_dim / 8 lanes per cached row (8 values
+//    each), a lane-group reduction per score, scores staged in LDS.
 #include "bfp_attn.hpp"
 #include "bfp_device.hpp"
 #include "bfp_encode.hpp"
@@ -387,24 +386,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(ChunkArgs ca) 
   }
 }
 
-// Matrix-core variant for G = 8 query heads per KV head, on the fp32 matrix instruction
-// (v_mfma_f32_16x16x4f32: D[16x16] += A[16x4] B[4x16]; lane l supplies A[l%16][l/16] and
-// B[l/16][l%16] and holds D[4 (l/16) + i][l%16], i < 4). Inputs stay fp32 as in the ALU kernel.
-// Each wave takes tiles of 16 tokens (tiles wave, wave + 4, ... of the chunk):
-//  * scores S^T = K Q^T: lane (j = l/16, r = l%16) supplies token r's dimensions
-//    [HD/4 j, HD/4 (j+1)) one per step (a contiguous HD/4-byte piece of its row) as A, and the
+// Matrix-core chunk kernel for G = 8 query heads per KV head. A 16x16 product D += A B on the
+// matrix instructions has lane l = 16 j + r (j < 4, r < 16) supply row r of A and column r of
+// B for the k slots of lane group j, and hold D[4 j + i][r], i < 4. Each wave takes tiles of 16
+// tokens (tiles wave, wave + 4, ... of the chunk):
+//  * scores S^T = K Q^T on v_mfma_f32_16x16x32_bf16: lane (j, r) supplies token r's dimensions
+//    [HD/4 j, HD/4 (j+1)), 8 per step (a contiguous HD/4-byte piece of its row), as A, and the
 //    same dimensions of query head r (zero for r >= 8) as B; D gives lane (j, r) the scores of
-//    tokens 4 j + i for head r;
-//  * the chunk's maximum per head (over lanes, then waves through LDS), p = exp(s - m) in place;
-//  * O = P V: step u takes the tokens 4 j + u of a tile, so lane (j, r) supplies its own p of
-//    register u as A, and as B the dimensions [HD/16 r, HD/16 (r+1)) of that token's value
-//    row (one whole 16-value block at HD = 256), one output tile per dimension of the piece.
-// The partial sums of the waves are added in wave order, as in the ALU kernel.
+//    tokens 4 j + i for head r. Decoded keys are exact in bf16; the scaled query is the sum of
+//    three bf16 parts (about 24 significant bits), one product each;
+//  * the wave's maximum per head (across the four lane groups), p = exp(s - m) in place;
+//  * O = P V on v_mfma_f32_16x16x16_bf16, k = the tile's 16 tokens: lane (j, r) supplies its
+//    own p (tokens 4 j + i, head r) as A, split into hi + lo bf16 parts, and as B the dims
+//    [HD/16 r, HD/16 (r+1)) of those four tokens' value rows (one whole 16-value block at
+//    HD = 256), one output tile per dimension of the piece.
+// The waves' (m, l, O) are combined in wave order.
 constexpr int kMfmaTile = 16;
-#ifndef ATTN_PREFETCH
-#define ATTN_PREFETCH 1
-#endif
-constexpr int kPrefetch = ATTN_PREFETCH;         // tiles whose rows are in flight ahead of use
 
 // Raw cached rows of one lane: a tile's key piece, a value piece (codes and exponent bytes).
 template <int HD>
@@ -478,45 +475,30 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
     qs[2][h][d] = (uint16_t)lo;
   }
 
-  // one pass over the wave's tiles with a running maximum m (head r) and, per lane, a running
-  // sum l of its own probabilities; the keys and values of the tile kPrefetch ahead load during
-  // this tile
+  // the wave's tiles in two phases: all scores (each tile's value rows load as soon as its key
+  // rows are used), the wave's maximum m (head r) and, per lane, the sum l of its own
+  // probabilities, then O = P V
   KPiece<HD> kb[NT];
   VPiece vb[NT][4];
-  // (no load sits in a branch: a branch lets the compiler place the use of the result, and so a
-  // wait for it, right after the load)
-  auto load_tile = [&](int tt) {
-    const int tile = wave + tt * kAttnWaves;
-    kload(tile, kb[tt]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) vload(tile, u, vb[tt][u]);
-  };
-#pragma unroll
-  for (int p = 0; p < kPrefetch; ++p) load_tile(p);
-  __syncthreads();                               // queries in LDS
+  for (int tt = 0; tt < NT; ++tt) kload(wave + tt * kAttnWaves, kb[tt]);
+  __syncthreads();                               // query parts in LDS
 
-  float m = -__builtin_inff(), l = 0.f;
-  f32x4 O[DPC];
-#pragma unroll
-  for (int n = 0; n < DPC; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float S[NT][4];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     const int tile = wave + tt * kAttnWaves;
-    if (tt + kPrefetch < NT) load_tile(tt + kPrefetch);
-    const KPiece<HD>& kc = kb[tt];
-    const VPiece (&vc)[4] = vb[tt];
-    // scores of tokens 4 j + i, head r
-    const uint32_t* code = reinterpret_cast<const uint32_t*>(kc.c);
-    // bf16 products (v_mfma_f32_16x16x32_bf16, A = 8 key values of lane group j, B = the
-    // same dims of query head r): the keys are exact in bf16 (at most 8 significant bits, the
-    // block scale a power of two), the query is the sum of its three parts; per part an
-    // accumulator of its own, added at the end
+    // scores of tokens 4 j + i, head r: bf16 products (v_mfma_f32_16x16x32_bf16, A = 8 key
+    // values of lane group j, B = the same dims of query head r): the keys are exact in bf16
+    // (at most 8 significant bits, the block scale a power of two), the query is the sum of
+    // its three parts; per part an accumulator of its own, added at the end
+    const uint32_t* code = reinterpret_cast<const uint32_t*>(kb[tt].c);
     f32x4 acc[3];
 #pragma unroll
     for (int e = 0; e < 3; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < QK / 8; ++st) {
-      const float scl = block_scale<8>((kc.e >> (8 * (st / 2))) & 0xffu);
+      const float scl = block_scale<8>((kb[tt].e >> (8 * (st / 2))) & 0xffu);
       const uint32_t c0 = code[2 * st], c1 = code[2 * st + 1];
       float kv[8];
       mag4_bfp8(c0, kv);
@@ -528,52 +510,54 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
       kp2[1] = signed_pair(kv[2], kv[3], c0, c0, sign_sel(2, 7));
       kp2[2] = signed_pair(kv[4], kv[5], c1, c1, sign_sel(0, 5));
       kp2[3] = signed_pair(kv[6], kv[7], c1, c1, sign_sel(2, 7));
-      const bf16x8 kb = __builtin_bit_cast(bf16x8, kp2);
+      const bf16x8 kbf = __builtin_bit_cast(bf16x8, kp2);
 #pragma unroll
       for (int e = 0; e < 3; ++e) {
         const bf16x8 qb = *reinterpret_cast<const bf16x8*>(&qs[e][r][QK * j + 8 * st]);
-        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, acc[e], 0, 0, 0);
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbf, qb, acc[e], 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vload(tile, u, vb[tt][u]);
     const f32x4 as = acc[0] + (acc[1] + acc[2]);
-    float S[4] = {as.x, as.y, as.z, as.w};
-    float tmax = -__builtin_inff();
+    const float av[4] = {as.x, as.y, as.z, as.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[tt][i] = (r < G && tile * kMfmaTile + 4 * j + i < nt) ? av[i] : -__builtin_inff();
+  }
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, S[tt][i]);
+  m = fmaxf(m, __shfl_xor(m, 16, kWave));
+  m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  float l = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      S[i] = (r < G && tile * kMfmaTile + 4 * j + i < nt) ? S[i] : -__builtin_inff();
-      tmax = fmaxf(tmax, S[i]);
+      S[tt][i] = S[tt][i] == -__builtin_inff() ? 0.f : __expf(S[tt][i] - m);
+      l += S[tt][i];
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = mn == -__builtin_inff() ? 1.f : __expf(m - mn);
-    m = mn;
-    l *= alpha;
+
+  f32x4 O[DPC];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      S[i] = S[i] == -__builtin_inff() ? 0.f : __expf(S[i] - mn);
-      l += S[i];
-    }
-    // O rows are heads 4 j + i: their factors come from lanes r = 4 j + i (skipped when no
-    // head's maximum moved)
-    if (__any(alpha != 1.f)) {
+  for (int n = 0; n < DPC; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float f = __shfl(alpha, (4 * j + i) & 15, kWave);
-#pragma unroll
-        for (int n = 0; n < DPC; ++n) O[n][i] *= f;
-      }
-    }
+  for (int tt = 0; tt < NT; ++tt) {
+    const VPiece (&vc)[4] = vb[tt];
     // O += P V on v_mfma_f32_16x16x16_bf16 over the tile's 16 tokens: lane (j, r) supplies as
     // A its own probabilities (tokens 4 j + i, head r) as hi + lo bf16 parts, and as B the
     // value dims DPC r + n of those four tokens (exact in bf16), one product per n
     uint32_t ph[2], pl[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const uint32_t h0 = __float_as_uint(S[2 * e]) & 0xffff0000u, h1 = __float_as_uint(S[2 * e + 1]) & 0xffff0000u;
+      const uint32_t h0 = __float_as_uint(S[tt][2 * e]) & 0xffff0000u;
+      const uint32_t h1 = __float_as_uint(S[tt][2 * e + 1]) & 0xffff0000u;
       ph[e] = h1 | (h0 >> 16);
-      const uint32_t l0 = f32_to_bf16_rne(S[2 * e] - __uint_as_float(h0));
-      const uint32_t l1 = f32_to_bf16_rne(S[2 * e + 1] - __uint_as_float(h1));
+      const uint32_t l0 = f32_to_bf16_rne(S[tt][2 * e] - __uint_as_float(h0));
+      const uint32_t l1 = f32_to_bf16_rne(S[tt][2 * e + 1] - __uint_as_float(h1));
       pl[e] = (l1 << 16) | l0;
     }
     const s16x4 pah = __builtin_bit_cast(s16x4, ph), pal = __builtin_bit_cast(s16x4, pl);
@@ -604,20 +588,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
     }
 #pragma unroll
     for (int n = 0; n < DPC; ++n) {
-      uint32_t vb[2];
+      uint32_t vbf[2];
       if constexpr (V4R) {
-        vb[0] = __builtin_amdgcn_perm(__float_as_uint(vv[1][n]), __float_as_uint(vv[0][n]), 0x07060302u);
-        vb[1] = __builtin_amdgcn_perm(__float_as_uint(vv[3][n]), __float_as_uint(vv[2][n]), 0x07060302u);
+        vbf[0] = __builtin_amdgcn_perm(__float_as_uint(vv[1][n]), __float_as_uint(vv[0][n]), 0x07060302u);
+        vbf[1] = __builtin_amdgcn_perm(__float_as_uint(vv[3][n]), __float_as_uint(vv[2][n]), 0x07060302u);
       } else {
         const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vc[0].c);
         const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vc[1].c);
         const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vc[2].c);
         const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vc[3].c);
         const uint32_t sel = sign_sel(n % 4, 4 + n % 4);
-        vb[0] = signed_pair(vv[0][n], vv[1][n], w0[n / 4], w1[n / 4], sel);
-        vb[1] = signed_pair(vv[2][n], vv[3][n], w2[n / 4], w3[n / 4], sel);
+        vbf[0] = signed_pair(vv[0][n], vv[1][n], w0[n / 4], w1[n / 4], sel);
+        vbf[1] = signed_pair(vv[2][n], vv[3][n], w2[n / 4], w3[n / 4], sel);
       }
-      const s16x4 bv = __builtin_bit_cast(s16x4, vb);
+      const s16x4 bv = __builtin_bit_cast(s16x4, vbf);
       O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pah, bv, O[n], 0, 0, 0);
       O[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pal, bv, O[n], 0, 0, 0);
     }
