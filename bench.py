@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--pmc-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of --pmc-driver "
                          "into the traffic summary")
+    ap.add_argument("--attn-driver", action="store_true",
+                    help="only time the decode-attention workloads and print their lines (run under rocprofv3)")
     ap.add_argument("--kernel-summary", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace output folder into a per-kernel markdown table")
     return ap.parse_args()
@@ -165,6 +167,8 @@ def short_kernel_name(name: str) -> str:
     n = n[:cut]
     n = re.sub(r"\(anonymous namespace\)::", "", n)
     n = re.sub(r"\b(bfp|at::native|std|gemv_detail|mg|am)::", "", n)
+    if len(n) > 100:                     # library kernels with lambda-laden template arguments
+        n = n[:n.index("<")] + "<...>" if "<" in n else n[:100] + "..."
     return n
 
 
@@ -460,6 +464,9 @@ def main():
         sys.exit(2)
     if args.pmc_driver:
         pmc_driver()
+        return
+    if args.attn_driver:
+        print(json.dumps(attn_workloads(args)), flush=True)
         return
     import torch
     import block_float_quantized_amd as bfq
