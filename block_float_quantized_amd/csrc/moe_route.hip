@@ -135,20 +135,27 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
   double sel_l[8];
   int sel_e[8];
   for (int j = 0; j < a.top_k; ++j) {
-    // best candidate of this lane
-    double bv = -__builtin_huge_val();
-    int bi = 0x7fffffff;
+    // the largest remaining logit M (a max-reduction: exact, order-free), then the smallest
+    // expert index holding it: expert 64 q + lane, so the first q with a match, then its lowest
+    // lane (equality ballots, no divergent branch)
+    double bv = fmax(fmax(v[0], v[1]), fmax(v[2], v[3]));
+    bv = fmax(bv, dpp_f64<kDppQuadXor1>(bv));
+    bv = fmax(bv, dpp_f64<kDppQuadXor2>(bv));
+    bv = fmax(bv, dpp_f64<kDppHalfMirror>(bv));
+    bv = fmax(bv, dpp_f64<kDppRowRor8>(bv));
+    const double M = fmax(fmax(readlane_f64(bv, 0), readlane_f64(bv, 16)),
+                          fmax(readlane_f64(bv, 32), readlane_f64(bv, 48)));
+    int bi = -1;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      if (ix[q] < a.n_exp && (v[q] > bv || (v[q] == bv && ix[q] < bi))) { bv = v[q]; bi = ix[q]; }
+      const uint64_t b = __ballot(ix[q] < a.n_exp && v[q] == M);
+      if (bi < 0 && b != 0) bi = 64 * q + __builtin_ctzll(b);
     }
-    // wave argmax with the same order
-    wave_argmax(bv, bi);
-    sel_l[j] = bv;
+    sel_l[j] = M;
     sel_e[j] = bi;
 #pragma unroll
     for (int q = 0; q < kPer; ++q)
-      if (ix[q] == bi) { v[q] = -__builtin_huge_val(); ix[q] = 0x7fffffff; }
+      if (ix[q] == bi) v[q] = -__builtin_huge_val();
   }
   // lane j < top_k: exp(l_j - l_0) in fp64; the sum is taken in rank order (a fixed order)
   double ex = 0.0;

@@ -205,7 +205,8 @@ size_t bfp_moe_route_workspace_bytes(const bfp_moe_layer *L, int64_t m);
  * x: device bf16 [m][hidden]; ids: device int32 [m][top_k]; w: device fp32 [m][top_k];
  * g: device fp32 [m] or NULL; ws: device workspace of at least
  * bfp_moe_route_workspace_bytes(L, m) bytes. Only the router fields of L are read.
- * m > BFP_GEMM_MAX_M needs hidden % 64 == 0 (else BFP_E_UNSUPPORTED).
+ * m > BFP_GEMM_MAX_M needs hidden % 64 == 0 (else BFP_E_UNSUPPORTED). Inputs must be finite
+ * (a token whose logits hold Inf or NaN gets an unspecified selection).
  */
 int32_t bfp_moe_route(const bfp_moe_layer *L, const uint16_t *x, int64_t m,
                       int32_t *ids, float *w, float *g, void *ws, size_t ws_bytes, void *stream);
