@@ -307,6 +307,23 @@ __device__ __forceinline__ void dispatch_block(const DispatchArgs& a, DispLds<MA
   expert_scan(a, cnt, off, wtot, true);
   if (tid < E) a.counts[tid] = cnt[tid];
   if (tid <= E) a.offsets[tid] = off[tid];
+  if (a.m <= 32) {
+    // at most 32 tokens: one bitmap word per expert, a token's rank among the expert's tokens
+    // is the popcount of the lower bits (the general path below with a single word)
+    if (tid < 256) bitmap[tid][0] = 0;
+    __syncthreads();
+    if (tid < a.m)
+      for (int j = 0; j < K; ++j) atomicOr(&bitmap[eid[tid * K + j]][0], 1u << tid);
+    __syncthreads();
+    if (tid < a.m)
+      for (int j = 0; j < K; ++j) {
+        const int e = eid[tid * K + j];
+        const int pos = off[e] + __popc(bitmap[e][0] & ((1u << tid) - 1u));
+        a.perm[pos] = tid * K + j;
+        if (a.inv) a.inv[tid * K + j] = pos;
+      }
+    return;
+  }
   for (int c0 = 0; c0 < a.m; c0 += kDispThreads) {
     for (int i = tid; i < 256 * 32; i += kDispThreads) bitmap[i / 32][i % 32] = 0;
     __syncthreads();

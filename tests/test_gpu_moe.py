@@ -63,7 +63,7 @@ def test_route_special_cases():
     assert ids.cpu().tolist() == [chosen] * 3
 
 
-@pytest.mark.parametrize("m", [1, 7, 300, 2048, 5000])
+@pytest.mark.parametrize("m", [1, 7, 32, 33, 300, 2048, 5000])
 def test_dispatch_bit_exact(m):
     note(f"dispatch m={m}")
     rng = np.random.default_rng(m)
