@@ -92,20 +92,36 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouteArgs a) {
   const uint16_t* xr = a.x + (int64_t)t * a.hidden;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   const int chunks = a.hidden / 8;
-  for (int c = lane; c < chunks; c += 64) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(xr + c * 8);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  const uint16_t* wr[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = e0 + q;
-      if (e >= rows) break;
-      const uint16_t* wr = (e < a.n_exp) ? a.router_w + (int64_t)e * a.hidden : a.sh_gate_w;
-      const uint4 wv = *reinterpret_cast<const uint4*>(wr + c * 8);
-      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+  for (int q = 0; q < 4; ++q) {
+    const int e = min(e0 + q, rows - 1);       // rows past the end re-read the last one, unused
+    wr[q] = (e < a.n_exp) ? a.router_w + (int64_t)e * a.hidden : a.sh_gate_w;
+  }
+  // kU chunks per lane in flight: every load of a batch is issued (clamped to the row, no
+  // branch) before any product; the sums keep the chunk order
+  constexpr int kU = 4;
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kU) {
+    uint4 xv[kU], wv[kU][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[q] = __builtin_fma((double)bf16_lo(xw[i]), (double)bf16_lo(ww[i]), acc[q]);
-        acc[q] = __builtin_fma((double)bf16_hi(xw[i]), (double)bf16_hi(ww[i]), acc[q]);
+    for (int u = 0; u < kU; ++u) {
+      const int c = min(c0 + 64 * u, chunks - 1);
+      xv[u] = *reinterpret_cast<const uint4*>(xr + c * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wv[u][q] = *reinterpret_cast<const uint4*>(wr[q] + c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (c0 + 64 * u >= chunks) break;
+      const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t ww[4] = {wv[u][q].x, wv[u][q].y, wv[u][q].z, wv[u][q].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[q] = __builtin_fma((double)bf16_lo(xw[i]), (double)bf16_lo(ww[i]), acc[q]);
+          acc[q] = __builtin_fma((double)bf16_hi(xw[i]), (double)bf16_hi(ww[i]), acc[q]);
+        }
       }
     }
   }
