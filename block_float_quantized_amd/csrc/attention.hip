@@ -737,9 +737,6 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(ChunkArgs ca)
   }
 }
 
-template <int HD>
-constexpr int tokens_per_step() { return kAttnWaves * (kWave / (HD / 8)); }
-
 // Tokens per workgroup: about 256 workgroups in all, a multiple of 64 between 64 and kMaxChunk
 // (a whole number of steps of either kernel).
 inline int pick_chunk(int head_dim, int kv_heads, int L) {
