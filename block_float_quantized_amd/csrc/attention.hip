@@ -400,7 +400,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_chunk_kernel(ChunkArgs ca) 
 //    own p (tokens 4 j + i, head r) as A, split into hi + lo bf16 parts, and as B the dims
 //    [HD/16 r, HD/16 (r+1)) of those four tokens' value rows (one whole 16-value block at
 //    HD = 256), one output tile per dimension of the piece.
-// The waves' (m, l, O) are combined in wave order.
+// The waves' (m, l, O) are combined in wave order. The query parts and the waves' partial
+// outputs share one LDS area (33 KB at head_dim 256), and at most two tiles of value rows are
+// held in registers, so that the rotated-V kernel (4-bit value rows) runs 3 waves per SIMD;
+// the BFP8 one, with twice the value bytes per lane, stays at 2 (at 3 it spills).
 constexpr int kMfmaTile = 16;
 
 // Raw cached rows of one lane: a tile's key piece, a value piece (codes and exponent bytes).
@@ -416,13 +419,16 @@ struct VPiece {
 
 // NT: tiles per wave (the chunk is 64 NT tokens).
 template <int HD, bool V4R, int NT>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkArgs ca) {
+__global__ __launch_bounds__(kAttnThreads, V4R ? 3 : 2) void attn_chunk_mfma_kernel(ChunkArgs ca) {
   constexpr int G = 8;
   constexpr int QK = HD / 4;                     // score steps; dims per lane group
   constexpr int DPC = HD / 16;                   // value dims per lane column = output tiles
   constexpr int QS = HD + 8;                     // LDS row stride of the query parts (conflict-free b128 reads)
-  __shared__ float red[kAttnWaves][G][HD];
-  __shared__ __align__(16) uint16_t qs[3][16][QS];
+  // one LDS area: the query parts while scores run, then the waves' partial outputs
+  constexpr int kQsBytes = 3 * 16 * QS * 2, kRedBytes = kAttnWaves * G * HD * 4;
+  __shared__ __align__(16) unsigned char lds_area[kQsBytes > kRedBytes ? kQsBytes : kRedBytes];
+  auto& qs = *reinterpret_cast<uint16_t (*)[3][16][QS]>(lds_area);
+  auto& red = *reinterpret_cast<float (*)[kAttnWaves][G][HD]>(lds_area);
   __shared__ float wstat[kAttnWaves][16], wsum[kAttnWaves][16], wfac[kAttnWaves][G];
   __shared__ float mrow[G], lrow[G];
   const AttnArgs& a = ca.a;
@@ -517,8 +523,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
         acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbf, qb, acc[e], 0, 0, 0);
       }
     }
+    if (tt == (NT >= 2 ? NT - 2 : 0))          // the first tile's value rows, shortly before P V
 #pragma unroll
-    for (int u = 0; u < 4; ++u) vload(tile, u, vb[tt][u]);
+      for (int u = 0; u < 4; ++u) vload(wave, u, vb[0][u]);
     const f32x4 as = acc[0] + (acc[1] + acc[2]);
     const float av[4] = {as.x, as.y, as.z, as.w};
 #pragma unroll
@@ -546,6 +553,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
   for (int n = 0; n < DPC; ++n) O[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
+    if (tt + 1 < NT)                             // the next tile's value rows load during this one
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vload(wave + (tt + 1) * kAttnWaves, u, vb[tt + 1][u]);
     const VPiece (&vc)[4] = vb[tt];
     // O += P V on v_mfma_f32_16x16x16_bf16 over the tile's 16 tokens: lane (j, r) supplies as
     // A its own probabilities (tokens 4 j + i, head r) as hi + lo bf16 parts, and as B the
@@ -610,6 +620,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_chunk_mfma_kernel(ChunkA
   l += __shfl_xor(l, 32, kWave);
 
   // the waves' (m, l, O) combined in wave order: M = max m_w, O = sum_w e^(m_w - M) O_w
+  __syncthreads();                               // every wave is done with the query parts
   if (j == 0) {
     wstat[wave][r] = m;
     wsum[wave][r] = l;
