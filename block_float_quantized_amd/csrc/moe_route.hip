@@ -51,34 +51,21 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
+// wave-wide maximum (fp64 max is exact, so the combination order does not matter)
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = fmax(v, dpp_f64<kDppQuadXor1>(v));
+  v = fmax(v, dpp_f64<kDppQuadXor2>(v));
+  v = fmax(v, dpp_f64<kDppHalfMirror>(v));
+  v = fmax(v, dpp_f64<kDppRowRor8>(v));
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
   v += dpp_f64<kDppQuadXor1>(v);
   v += dpp_f64<kDppQuadXor2>(v);
   v += dpp_f64<kDppHalfMirror>(v);
   v += dpp_f64<kDppRowRor8>(v);
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
-}
-
-// (value, index) pairs ordered by value descending, then index ascending
-__device__ __forceinline__ void better_of(double& bv, int& bi, double ov, int oi) {
-  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-}
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(double& bv, int& bi) {
-  better_of(bv, bi, dpp_f64<CTRL>(bv), dpp_i32<CTRL>(bi));
-}
-// wave-wide best (value, index); every lane gets the result
-__device__ __forceinline__ void wave_argmax(double& bv, int& bi) {
-  argmax_step<kDppQuadXor1>(bv, bi);
-  argmax_step<kDppQuadXor2>(bv, bi);
-  argmax_step<kDppHalfMirror>(bv, bi);
-  argmax_step<kDppRowRor8>(bv, bi);
-  double v = readlane_f64(bv, 0);
-  int i = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) better_of(v, i, readlane_f64(bv, 16 * r), __builtin_amdgcn_readlane(bi, 16 * r));
-  bv = v;
-  bi = i;
 }
 
 // One wave per (token, 4 experts). Expert index n_exp is the shared-expert gate row.
@@ -154,13 +141,7 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
     // the largest remaining logit M (a max-reduction: exact, order-free), then the smallest
     // expert index holding it: expert 64 q + lane, so the first q with a match, then its lowest
     // lane (equality ballots, no divergent branch)
-    double bv = fmax(fmax(v[0], v[1]), fmax(v[2], v[3]));
-    bv = fmax(bv, dpp_f64<kDppQuadXor1>(bv));
-    bv = fmax(bv, dpp_f64<kDppQuadXor2>(bv));
-    bv = fmax(bv, dpp_f64<kDppHalfMirror>(bv));
-    bv = fmax(bv, dpp_f64<kDppRowRor8>(bv));
-    const double M = fmax(fmax(readlane_f64(bv, 0), readlane_f64(bv, 16)),
-                          fmax(readlane_f64(bv, 32), readlane_f64(bv, 48)));
+    const double M = wave_max_f64(fmax(fmax(v[0], v[1]), fmax(v[2], v[3])));
     int bi = -1;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
@@ -671,17 +652,19 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
   // k-th largest lower end
   double lk = __builtin_huge_val();
   {
+    // per round: the largest remaining lower end (exact max-reduction), removed once from the
+    // lowest lane holding it (its first slot holding it); no divergent branch
     double v[4] = {lo[0], lo[1], lo[2], lo[3]};
     for (int j = 0; j < a.top_k; ++j) {
-      double bv = -__builtin_huge_val();
-      int bq = -1;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) if (v[q] > bv) { bv = v[q]; bq = q; }
-      double mv = bv;
-      int ml = lane;
-      wave_argmax(mv, ml);
+      const double bv = fmax(fmax(v[0], v[1]), fmax(v[2], v[3]));
+      const double mv = wave_max_f64(bv);
       lk = mv;
-      if (lane == ml && bq >= 0) v[bq] = -__builtin_huge_val();
+      const uint64_t b = __ballot(bv == mv);
+      const int ml = b ? __builtin_ctzll(b) : -1;
+      bool done = lane != ml;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (!done && v[q] == mv) { v[q] = -__builtin_huge_val(); done = true; }
     }
   }
   // candidates, in expert order
@@ -731,17 +714,24 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
   double sel_l[8];
   int sel_e[8];
   for (int j = 0; j < a.top_k; ++j) {
-    double bv = -__builtin_huge_val();
+    // the largest remaining exact logit, then the first candidate holding it: candidates are
+    // in expert order, candidate 64 q + lane, so the first q with a match and its lowest lane
+    const double M = wave_max_f64(fmax(fmax(v[0], v[1]), fmax(v[2], v[3])));
+    int bq = -1, bl = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t b = __ballot(ix[q] != 0x7fffffff && v[q] == M);
+      if (bq < 0 && b != 0) { bq = q; bl = __builtin_ctzll(b); }
+    }
     int bi = 0x7fffffff;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (ix[q] != 0x7fffffff && (v[q] > bv || (v[q] == bv && ix[q] < bi))) { bv = v[q]; bi = ix[q]; }
-    wave_argmax(bv, bi);
-    sel_l[j] = bv;
+      if (q == bq) bi = __builtin_amdgcn_readlane(ix[q], bl);
+    sel_l[j] = M;
     sel_e[j] = bi;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (ix[q] == bi) { v[q] = -__builtin_huge_val(); ix[q] = 0x7fffffff; }
+      if (q == bq && lane == bl) { v[q] = -__builtin_huge_val(); ix[q] = 0x7fffffff; }
   }
   double ex = 0.0, lj = sel_l[0];
   int ej = sel_e[0];
