@@ -238,6 +238,65 @@ def timed(fn, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
+def timed_graph(fn, outs, calls: int = 64, reps: int = 10):
+    """Device time per call of short, launch-bound calls: `calls` calls of fn(i) captured once
+    into a HIP graph (torch.cuda.CUDAGraph) and replayed `reps` times, so that host overhead
+    between launches drops out. First, three replays, each after eager work (the outputs
+    zeroed) and a synchronisation, must leave every output tensor in `outs` bit-identical to
+    an eager run of the same calls; else (or if capture fails) None."""
+    import torch
+    try:
+        torch.cuda.synchronize()
+        for i in range(calls):
+            fn(i)
+        torch.cuda.synchronize()
+        ref = [o.clone() for o in outs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                fn(i)
+        for _ in range(3):
+            for o in outs:
+                o.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for o, r in zip(outs, ref):
+                if not torch.equal(o.view(torch.uint8), r.view(torch.uint8)):
+                    log("graph replay differs from the eager calls; graph timing skipped")
+                    return None
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream()
+        t0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / (reps * calls)
+        del g
+        return ms
+    except RuntimeError as e:
+        log(f"graph timing skipped: {e}")
+        return None
+
+
+def add_graph_timing(entry: dict, fn, outs, nbytes: int):
+    """Adds the graph-replay time (see timed_graph) and its rate to a workload entry."""
+    ms = timed_graph(fn, outs)
+    if ms is None:
+        entry["us_per_call_graph"] = None
+        return
+    entry["us_per_call_graph"] = round(ms * 1e3, 2)
+    entry["GB/s_graph"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    entry["pct_hbm_peak_graph"] = round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)
+
+
 # ---- headline: dense BFP4 MLP decode ------------------------------------------------------
 
 def mlp_bytes(m: int) -> dict:
@@ -325,24 +384,28 @@ def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32", argmax_name=None
         x = bf16_dev(xb)
         y = torch.empty((m, base.n), dtype=torch.float32, device="cuda")
         ws = workspace(bfq.bfp_gemm_workspace_bytes(base, m))
-        ms = timed(lambda i: bfq.bfp_gemm(mats[i % R], x, out=y, workspace=ws), args.steps, args.warmup)
+        fn = lambda i: bfq.bfp_gemm(mats[i % R], x, out=y, workspace=ws)
+        ms = timed(fn, args.steps, args.warmup)
         nbytes = base.nbytes + m * base.k * 2 + m * base.n * 4
         out[f"{name} M={m}"] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                 "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                                 "bytes": nbytes, "replicas": R, "tok_per_s": round(m / (ms * 1e-3), 1)}
-        log(f"{name} M={m}: {ms * 1e3:.2f} us")
+        add_graph_timing(out[f"{name} M={m}"], fn, [y], nbytes)
+        log(f"{name} M={m}: {ms * 1e3:.2f} us (graph replay {out[f'{name} M={m}']['us_per_call_graph']} us)")
         if argmax_name:
             idx = torch.empty((m,), dtype=torch.int32, device="cuda")
             val = torch.empty((m,), dtype=torch.float32, device="cuda")
             ws = workspace(bfq.bfp_gemm_argmax_workspace_bytes(base, m))
-            ms = timed(lambda i: bfq.bfp_gemm_argmax(mats[i % R], x, idx=idx, val=val, workspace=ws),
-                       args.steps, args.warmup)
+            fa = lambda i: bfq.bfp_gemm_argmax(mats[i % R], x, idx=idx, val=val, workspace=ws)
+            ms = timed(fa, args.steps, args.warmup)
             nbytes = base.nbytes + m * base.k * 2 + m * 8
             out[f"{argmax_name} M={m}"] = {"us_per_call": round(ms * 1e3, 2),
                                            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                            "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                                            "bytes": nbytes, "replicas": R, "tok_per_s": round(m / (ms * 1e-3), 1)}
-            log(f"{argmax_name} M={m}: {ms * 1e3:.2f} us")
+            add_graph_timing(out[f"{argmax_name} M={m}"], fa, [idx, val], nbytes)
+            log(f"{argmax_name} M={m}: {ms * 1e3:.2f} us "
+                f"(graph replay {out[f'{argmax_name} M={m}']['us_per_call_graph']} us)")
     del mats
     torch.cuda.empty_cache()
     return out
@@ -375,14 +438,16 @@ def attn_workloads(args):
         q = torch.randn((hq, hd), device="cuda", generator=gen)
         y = torch.empty((hq, hd), dtype=torch.float32, device="cuda")
         ws = workspace(bfq.bfp_attn_decode_workspace_bytes(caches[0], hq, L))
-        ms = timed(lambda i: bfq.bfp_attn_decode(caches[i % R], q, L, 1.0 / 16, out=y, workspace=ws),
-                   args.steps, args.warmup)
-        out[f"{name} attention decode L={L}"] = {"us_per_call": round(ms * 1e3, 2),
-                                                 "GB/s": round(per / (ms * 1e-3) / 1e9, 1),
-                                                 "pct_hbm_peak": round(100 * per / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
-                                                 "cache_bytes": per, "replicas": R,
-                                                 "bytes_per_token_layer": kvh * row}
-        log(f"attention {name} L={L}: {ms * 1e3:.2f} us")
+        fn = lambda i: bfq.bfp_attn_decode(caches[i % R], q, L, 1.0 / 16, out=y, workspace=ws)
+        ms = timed(fn, args.steps, args.warmup)
+        key = f"{name} attention decode L={L}"
+        out[key] = {"us_per_call": round(ms * 1e3, 2),
+                    "GB/s": round(per / (ms * 1e-3) / 1e9, 1),
+                    "pct_hbm_peak": round(100 * per / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                    "cache_bytes": per, "replicas": R,
+                    "bytes_per_token_layer": kvh * row}
+        add_graph_timing(out[key], fn, [y], per)
+        log(f"attention {name} L={L}: {ms * 1e3:.2f} us (graph replay {out[key]['us_per_call_graph']} us)")
         del caches
         torch.cuda.empty_cache()
     return out
@@ -416,15 +481,17 @@ def moe_workloads(args):
         for s in range(8):
             bfq.bfp_moe_forward(layers[0], xs[s], out=y, workspace=ws, topk_ids=ids)
             distinct.append(len(np.unique(ids.cpu().numpy())))
-        ms = timed(lambda i: bfq.bfp_moe_forward(layers[i % nl], xs[i % 8], out=y, workspace=ws),
-                   args.steps, args.warmup)
+        fn = lambda i: bfq.bfp_moe_forward(layers[i % nl], xs[i % 8], out=y, workspace=ws)
+        ms = timed(fn, args.steps, args.warmup)
         d = float(np.mean(distinct))
         nbytes = d * expert_bytes + shared_bytes + router_bytes + m * 2048 * 2 + m * 2048 * 4
         out[f"moe decode M={m}"] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                     "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                                     "distinct_experts": d, "bytes": int(nbytes),
                                     "tok_per_s": round(m / (ms * 1e-3), 1)}
-        log(f"moe decode M={m}: {ms * 1e3:.2f} us, {d:.1f} experts")
+        add_graph_timing(out[f"moe decode M={m}"], fn, [y], int(nbytes))
+        log(f"moe decode M={m}: {ms * 1e3:.2f} us, {d:.1f} experts "
+            f"(graph replay {out[f'moe decode M={m}']['us_per_call_graph']} us)")
     # prefill chunk: 2,048 tokens with the skewed router bias
     bias = torch.from_numpy(synth.router_bias(0)).to("cuda")
     for L in layers:
