@@ -292,9 +292,11 @@ size_t bfp_attn_decode_workspace_bytes(const bfp_kv_cache *c, int32_t q_heads, i
  *   values, the sum rotated back by the same transform in fp32).
  * q: device [q_heads][head_dim], fp32 or bf16 (q_dtype); out: device fp32
  * [q_heads][head_dim]. q_heads / kv_heads must be 1, 2, 4 or 8 (else BFP_E_UNSUPPORTED).
- * Products and sums are fp32 (exp via the hardware exp2); the sequence is split into chunks
- * merged in a fixed order, so results are deterministic. ws: device workspace of at least
- * bfp_attn_decode_workspace_bytes bytes.
+ * Sums are fp32 (exp via the hardware exp2). With 8 query heads per KV head the products run
+ * on the bf16 matrix instructions: cached values are exact in bf16, the scaled query is the sum
+ * of three bf16 parts (~24 significant bits) and the probabilities of two (~16); otherwise the
+ * products are fp32. The sequence is split into chunks merged in a fixed order, so results are
+ * deterministic. ws: device workspace of at least bfp_attn_decode_workspace_bytes bytes.
  */
 int32_t bfp_attn_decode(const bfp_kv_cache *c, const void *q, int32_t q_dtype, int32_t q_heads,
                         int64_t seq_len, float scale, float *out, void *ws, size_t ws_bytes,
