@@ -58,6 +58,8 @@ def parse():
                          "into the traffic summary")
     ap.add_argument("--attn-driver", action="store_true",
                     help="only time the decode-attention workloads and print their lines (run under rocprofv3)")
+    ap.add_argument("--moe-driver", action="store_true",
+                    help="only time the MoE workloads (decode and the 2,048-token prefill) and print their lines")
     ap.add_argument("--kernel-summary", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace output folder into a per-kernel markdown table")
     return ap.parse_args()
@@ -538,6 +540,9 @@ def main():
         return
     if args.attn_driver:
         print(json.dumps(attn_workloads(args)), flush=True)
+        return
+    if args.moe_driver:
+        print(json.dumps(moe_workloads(args)), flush=True)
         return
     import torch
     import block_float_quantized_amd as bfq
