@@ -1,4 +1,5 @@
-// Internal interface of the BFP8 KV cache kernels (append, decode attention).
+// Internal interface of the BFP KV cache kernels (append, decode attention): BFP8 K and V, or
+// BFP8 K and 4-bit V after a Hadamard rotation.
 #pragma once
 
 #include <hip/hip_runtime.h>
