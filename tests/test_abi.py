@@ -131,3 +131,19 @@ def test_python_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(bfq, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         bfq.lib()
+
+
+def test_kv_cache_planes_and_format():
+    """Plane sizes of both cache formats (host tensors; no device call) and the format field
+    handed to the C struct."""
+    for fmt, vbytes in ((bfq.KV_V_BFP8, 256), (bfq.KV_V_BFP4_HADAMARD, 128)):
+        c = bfq.KvCache.empty(2, 256, 10, device="cpu", v_format=fmt)
+        assert c.k_exp.numel() == c.v_exp.numel() == 2 * 10 * 16
+        assert c.k_code.numel() == 2 * 10 * 256 and c.v_code.numel() == 2 * 10 * vbytes
+        with pytest.raises(ValueError):                 # the binding takes device memory only
+            c.view()
+        assert bfq._KvCache(2, 256, 10, 16, 16, 16, 16, fmt).v_format == fmt
+    # 26 / 34 of the BFP8 cache's bytes (the 27B card's 26,624 vs 34,816 bytes per token)
+    a = bfq.KvCache.empty(4, 256, 16, device="cpu").nbytes
+    b = bfq.KvCache.empty(4, 256, 16, device="cpu", v_format=bfq.KV_V_BFP4_HADAMARD).nbytes
+    assert b * 34 == a * 26
