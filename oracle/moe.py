@@ -14,7 +14,8 @@ Readings taken where the pages are silent:
 * Router logits l_e = sum_k x_k * Wr[e][k] (+ b_e when a per-expert bias is given), from
   exact bf16 x bf16 products summed in fp64.
 * Selection: the top-k experts by (logit descending, expert index ascending), reported
-  in that order.
+  in that order. Where fp64 rounding could decide it (two logits that the selection compares
+  closer than their error bound), the logits in question are recomputed exactly.
 * Weights: p = softmax over all experts; r_j = p[e_j] / sum of p over the selected
   experts (softmax restricted to the top-k, renormalised).
 * Shared-expert gate: g = sigmoid(x . g_s) with a bf16 vector g_s.
@@ -27,21 +28,65 @@ Readings taken where the pages are silent:
 """
 from __future__ import annotations
 
+from fractions import Fraction
+
 import numpy as np
 
 from .bfp import decode, encode
 from .linalg import bf16_round, bf16_to_f64, sigmoid, swiglu
 
 
+def _exact_logits(x_row: np.ndarray, w_rows: np.ndarray, bias: np.ndarray | None) -> list:
+    """Exact router logits as Fractions: every bf16 value is an integer multiple of 2**-133
+    (the smallest bf16 subnormal), so x_k * w_k * 2**266 is an integer and the sum over k is
+    exact in Python integers; a fp32 bias is added as the exact rational it is."""
+    xi = [int(v) for v in np.ldexp(x_row, 133)]
+    out = []
+    for e, w in enumerate(w_rows):
+        wi = [int(v) for v in np.ldexp(w, 133)]
+        f = Fraction(sum(a * b for a, b in zip(xi, wi) if a and b), 2 ** 266)
+        if bias is not None:
+            f += Fraction(float(bias[e]))
+        out.append(f)
+    return out
+
+
 def route(x_bits: np.ndarray, router_bits: np.ndarray, top_k: int = 8,
           bias: np.ndarray | None = None, sh_gate_bits: np.ndarray | None = None) -> dict:
-    """Router + top-k + renormalised softmax weights + shared-expert gate (fp64)."""
+    """Router + top-k + renormalised softmax weights + shared-expert gate (fp64).
+
+    The logits are fp64 sums of exact bf16 products, so each is within
+    d_e = 2 (n + 2) 2**-53 (sum_k |x_k w_k| + |b_e| + |l_e|) of its exact value (any
+    summation order). Per token, the experts that could still reach the top-k are those whose
+    upper end l_e + d_e is not below the k-th largest lower end; if any two of their intervals
+    overlap, the order among them is not settled by the fp64 values, and their logits are
+    recomputed exactly (``_exact_logits``) and replaced by the nearest doubles of the exact
+    values before the selection and the weights. The selection itself is a plain sort by
+    (logit descending, expert ascending).
+    """
     x = bf16_to_f64(x_bits)
     wr = bf16_to_f64(router_bits)
     logits = x @ wr.T
+    b64 = None
     if bias is not None:
-        logits = logits + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+        b64 = np.asarray(bias, dtype=np.float32).astype(np.float64)
+        logits = logits + b64[None, :]
     m, n_exp = logits.shape
+    n = x.shape[1]
+    a = np.abs(x) @ np.abs(wr).T
+    d = 2.0 * (n + 2) * 2.0 ** -53 * (a + np.abs(logits) + (np.abs(b64)[None, :] if b64 is not None else 0.0))
+    exact = np.zeros(m, dtype=bool)
+    for t in range(m):
+        lo, hi = logits[t] - d[t], logits[t] + d[t]
+        lk = np.sort(lo)[::-1][top_k - 1]              # k-th largest lower end
+        cand = np.nonzero(hi >= lk)[0]
+        lc, hc = lo[cand], hi[cand]
+        overlap = (lc[:, None] <= hc[None, :]) & (lc[None, :] <= hc[:, None])
+        np.fill_diagonal(overlap, False)
+        if overlap.any():
+            ex = _exact_logits(x[t], wr[cand], None if b64 is None else b64[cand])
+            logits[t, cand] = [float(f) for f in ex]
+            exact[t] = True
     ids = np.empty((m, top_k), np.int32)
     for t in range(m):
         order = sorted(range(n_exp), key=lambda e: (-logits[t, e], e))
@@ -51,7 +96,7 @@ def route(x_bits: np.ndarray, router_bits: np.ndarray, top_k: int = 8,
     p = p / p.sum(axis=1, keepdims=True)
     sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
     r = sel / sel.sum(axis=1, keepdims=True)
-    out = {"ids": ids, "r": r, "logits": logits}
+    out = {"ids": ids, "r": r, "logits": logits, "exact": exact}
     if sh_gate_bits is not None:
         out["g"] = sigmoid(x @ bf16_to_f64(sh_gate_bits))
     return out

@@ -114,6 +114,44 @@ def test_silu_and_swiglu():
     u = np.array([2.0, -1.0, 0.5, 1.0, 1.0, 3.0])
     assert np.allclose(oracle.swiglu(g, u), s * u, rtol=0, atol=0)
     assert oracle.linalg.sigmoid(np.array([0.0]))[0] == 0.5
+    # closed forms at g = +-ln 3, where e^-g is 1/3 or 3: silu(ln 3) = (3/4) ln 3,
+    # silu(-ln 3) = -(1/4) ln 3 (a sign slip in the exponent swaps the two)
+    l3 = math.log(3.0)
+    s3 = oracle.silu(np.array([l3, -l3]))
+    assert abs(s3[0] - 0.75 * l3) <= 4e-16 * l3 and abs(s3[1] + 0.25 * l3) <= 4e-16 * l3
+
+
+# logistic function values from 50-digit decimal arithmetic (1 / (1 + e^-z)), i.e. the
+# constants e/(1+e), 1/(1+e^2), ... of mathematical tables, not the oracle's own formula
+_SIGMOID_TABLE = {
+    1.0: 0.73105857863000487925,
+    2.0: 0.88079707797788244406,
+    -2.0: 0.11920292202211755594,
+    0.5: 0.62245933120185456464,
+    -40.0: 4.2483542552915889773e-18,
+}
+
+
+def test_sigmoid_pins():
+    """The shared-expert gate sigma(z) = 1 / (1 + e^-z): closed forms that a sign slip
+    (1 / (1 + e^z)), a missing term or a swapped branch fails."""
+    sig = oracle.linalg.sigmoid
+    for z, want in _SIGMOID_TABLE.items():
+        got = sig(np.array([z]))[0]
+        assert abs(got - want) <= 2.3e-16 * want, (z, got, want)
+    # sigma(ln k) = k / (k + 1) (e^-ln k = 1/k), on both sides of zero
+    for k in range(2, 12):
+        z = math.log(k)
+        got = sig(np.array([z, -z]))
+        assert abs(got[0] - k / (k + 1)) <= 4e-16 and abs(got[1] - 1 / (k + 1)) <= 4e-16 / (k + 1) * k
+    # limits: sigma(40) rounds to 1 in fp64, sigma(-40) = e^-40 (1 - e^-40 + ...) and never 0
+    assert sig(np.array([40.0]))[0] == 1.0
+    assert abs(sig(np.array([-40.0]))[0] - math.exp(-40.0)) <= 1e-15 * math.exp(-40.0)
+    assert sig(np.array([-745.0]))[0] > 0.0 and sig(np.array([800.0]))[0] == 1.0
+    # strictly increasing with sigma(z) > 1/2 for z > 0
+    z = np.linspace(-30, 30, 2001)
+    v = sig(z)
+    assert np.all(np.diff(v) > 0) and np.all(v[z > 0] > 0.5) and np.all(v[z < 0] < 0.5)
 
 
 def test_rel_err_zero_normaliser():

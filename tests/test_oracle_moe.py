@@ -50,6 +50,62 @@ def test_router_bias_forces_selection_and_order():
     assert np.all(np.diff(out["r"], axis=1) < 0)
 
 
+def test_router_shared_gate_values():
+    """The shared gate g = sigmoid(x . g_s) against tabulated logistic values: a one-hot x
+    makes x . g_s one exact bf16 value z, and sigma(1), sigma(-2) are the constants
+    e/(1+e) and 1/(1+e^2) (50-digit decimal arithmetic)."""
+    x = np.zeros((2, 64), np.uint16)
+    x[0, 5] = synth.bf16_bits(np.array([1.0], np.float32))[0]
+    x[1, 40] = synth.bf16_bits(np.array([-0.5], np.float32))[0]
+    gs = np.zeros(64, np.uint16)
+    gs[5] = synth.bf16_bits(np.array([1.0], np.float32))[0]
+    gs[40] = synth.bf16_bits(np.array([4.0], np.float32))[0]
+    wr = synth.normal_bf16(np.random.default_rng(0), (16, 64), std=0.02)
+    g = oracle.route(x, wr, 4, sh_gate_bits=gs)["g"]
+    assert abs(g[0] - 0.73105857863000487925) <= 2.3e-16
+    assert abs(g[1] - 0.11920292202211755594) <= 2.3e-16 * 0.12
+
+
+def test_router_near_tie_settled_exactly():
+    """Two logits whose fp64 sums come out in the wrong order: expert 0's exact logit is
+    2^60 + 1000 * 1 - 2^60 = 1000, expert 1's is 999 + 0.5 = 999.5. Summed in fp64 the ones
+    next to 2^60 are lost (the ulp there is 256), so a plain fp64 matmul ranks expert 1 first;
+    the oracle's error intervals overlap, it recomputes the logits exactly and ranks expert 0
+    first, with the weights of the exact logits (sigma(0.5) and 1 - sigma(0.5))."""
+    h = 1024
+    one, big, half = (synth.bf16_bits(np.array([v], np.float32))[0] for v in (1.0, 2.0 ** 30, 0.5))
+    nbig = synth.bf16_bits(np.array([-2.0 ** 30], np.float32))[0]
+    x = np.zeros((1, h), np.uint16)
+    x[0, 0], x[0, 1:1001], x[0, 1001] = big, one, big
+    wr = np.zeros((4, h), np.uint16)
+    wr[0, 0], wr[0, 1:1001], wr[0, 1001] = big, one, nbig
+    wr[1, 1:1000], wr[1, 1000] = one, half
+    plain = oracle.bf16_to_f64(x) @ oracle.bf16_to_f64(wr).T
+    assert plain[0, 1] > plain[0, 0], "the construction must fool a plain fp64 sum"
+    out = oracle.route(x, wr, 2)
+    assert out["exact"].tolist() == [True]
+    assert out["ids"].tolist() == [[0, 1]]
+    assert out["logits"][0, 0] == 1000.0 and out["logits"][0, 1] == 999.5
+    assert abs(out["r"][0, 0] - 0.62245933120185456464) <= 4e-16
+    assert abs(out["r"][0, 1] - 0.37754066879814543536) <= 4e-16
+    # with a fp32 bias of +0.75 on expert 1 the exact order flips (1000 < 1000.25)
+    bias = np.array([0.0, 0.75, 0.0, 0.0], np.float32)
+    out = oracle.route(x, wr, 2, bias=bias)
+    assert out["ids"].tolist() == [[1, 0]] and out["logits"][0, 1] == 1000.25
+
+
+def test_router_random_data_needs_no_recheck():
+    """On the workload's router draws the fp64 error intervals never overlap at the
+    selection, so the recheck leaves the plain fp64 ranking in place."""
+    router, shg = synth.moe_router(0)
+    x = synth.moe_tokens(64, 0)
+    out = oracle.route(x, router, 8, sh_gate_bits=shg)
+    assert not out["exact"].any()
+    plain = oracle.bf16_to_f64(x) @ oracle.bf16_to_f64(router).T
+    want = np.argsort(-plain, axis=1, kind="stable")[:, :8]
+    assert np.array_equal(out["ids"], want)
+
+
 def test_router_tiny_vs_exact():
     rng = np.random.default_rng(2)
     m, n_exp, h = 5, 12, 24
