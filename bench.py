@@ -16,7 +16,8 @@ last-level cache): the bandwidths are HBM numbers. Each timed loop runs W warm-u
 K calls between two events on the launch stream. Bandwidth = algorithmic bytes (packed
 weights actually read + activations in + outputs out) / time per call. The dominant kernel
 of the headline step (gate/up + SwiGLU GEMV) is timed alone over K back-to-back launches for
-the roofline entry. The CPU oracle is timed on a bounded sample of the headline step.
+the roofline entry. The CPU oracle is timed on the host: the headline step whole, and one
+call (or a bounded sample) of each other workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--M 1] [--quick]
 Prints one JSON line.
@@ -50,7 +51,6 @@ def parse():
     ap.add_argument("--M", type=int, default=1)
     ap.add_argument("--quick", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows per matrix in the CPU sample")
     ap.add_argument("--pmc-driver", action="store_true",
                     help="only launch the headline gate/up kernel and a 512 MiB copy (run under rocprofv3 --pmc)")
     ap.add_argument("--pmc-report", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -351,28 +351,139 @@ def run_mlp(args, m, mats, xb, batch_invariant=False, graph=False):
     return out
 
 
-def cpu_baseline(c: dict, rows: int, xbits: np.ndarray) -> dict:
-    """Time the CPU oracle (decode the packed bytes, fp64 GEMV, SwiGLU) on `rows` rows of each
-    matrix of the headline step, one thread."""
+def cpu_threads() -> int:
+    """Host threads the oracle may use: the cores this process may run on, capped by
+    OMP_NUM_THREADS when that is set (a GPU machine grants a share of its host)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(env)) if env.isdigit() and int(env) > 0 else n
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class _PackedBank:
+    """Expert weights as the oracle's packed bytes (encoded before timing); decoded on every
+    call like the GPU streams them."""
+
+    def __init__(self, layer: dict, experts):
+        import oracle
+        self.fmt, self.hidden, self.inter = 4, layer["hidden"], layer["inter"]
+        h, f = self.hidden, self.inter
+        self.packed = {}
+        for e in experts:
+            if e < 0:
+                mats = (layer["sh_gate"], layer["sh_up"], layer["sh_down"])
+            else:
+                mats = (layer["gate"][e * f:(e + 1) * f], layer["up"][e * f:(e + 1) * f],
+                        layer["down"][e * h:(e + 1) * h])
+            self.packed[e] = [(oracle.encode(w, 4), w.shape) for w in mats]
+        self.nbytes = sum(e_.nbytes + c_.nbytes for v in self.packed.values() for (e_, c_), _ in v)
+
+    def expert(self, e: int):
+        import oracle
+        return tuple(oracle.decode(ex, cc, 4, n, k) for (ex, cc), (n, k) in self.packed[int(e)])
+
+
+def cpu_baseline(c: dict, xbits: np.ndarray) -> dict:
+    """The CPU oracle timed on the host, one call per workload (the LM head and the prefill
+    chunk on a bounded sample): decode the packed bytes (encoded before timing, as the GPU's
+    weights are quantized before timing) and compute in fp64 with numpy, BLAS threads = the
+    host cores this process may use. The headline step is also timed on one thread."""
     import oracle
+    import synth
     from threadpoolctl import threadpool_limits
-    m = xbits.shape[0]
-    x = oracle.bf16_to_f64(xbits)
-    packed = {name: (oracle.encode(c[name][:rows], 4), c[name][:rows].shape) for name in ("wg", "wu", "wd")}
-    nbytes = sum(e.nbytes + cc.nbytes for (e, cc), _ in packed.values())
-    with threadpool_limits(limits=1):
-        t = time.perf_counter()
+    threads = cpu_threads()
+    out = {}
+
+    def mlp_step(packed, x):
         (eg, cg), (n, k) = packed["wg"]
         (eu, cu), _ = packed["wu"]
-        hh = oracle.swiglu(oracle.gemm(x, oracle.decode(eg, cg, 4, n, k)), oracle.gemm(x, oracle.decode(eu, cu, 4, n, k)))
+        h = oracle.swiglu(oracle.gemm(x, oracle.decode(eg, cg, 4, n, k)), oracle.gemm(x, oracle.decode(eu, cu, 4, n, k)))
         (ed, cd), (nd, kd) = packed["wd"]
-        hfull = np.zeros((m, kd))
-        hfull[:, :hh.shape[1]] = hh
-        oracle.gemm(hfull, oracle.decode(ed, cd, 4, nd, kd))
-        dt = time.perf_counter() - t
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} rows of gate, up and down at M={m}: decode packed BFP4 + fp64 GEMV + "
-                      f"SwiGLU, {nbytes / 1e6:.1f} MB of packed weights in {dt:.2f} s on 1 thread"}
+        return oracle.bf16_round(oracle.gemm(h, oracle.decode(ed, cd, 4, nd, kd)))
+
+    def clock(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    # dense MLP step at M = 1 (the headline workload), whole
+    packed = {name: (oracle.encode(c[name], 4), c[name].shape) for name in ("wg", "wu", "wd")}
+    wbytes = sum(e.nbytes + cc.nbytes for (e, cc), _ in packed.values())
+    x = oracle.bf16_to_f64(xbits)
+    nbytes = wbytes + xbits.size * 2 * 2
+    with threadpool_limits(limits=threads):
+        dt = clock(lambda: mlp_step(packed, x))
+    with threadpool_limits(limits=1):
+        dt1 = clock(lambda: mlp_step(packed, x))
+    out["dense BFP4 MLP M=1"] = {"us_per_call": round(dt * 1e6), "GB/s": round(nbytes / dt / 1e9, 4),
+                                 "GB/s_1_thread": round(nbytes / dt1 / 1e9, 4), "sample": "whole step"}
+    del packed
+    log(f"cpu oracle: MLP step {dt:.2f} s ({threads} threads), {dt1:.2f} s (1 thread)")
+    with threadpool_limits(limits=threads):
+        # single BFP8 GEMV 2048 x 2048, whole
+        g = synth.gemv_case(0)
+        (e, cc) = oracle.encode(g["w"], 8)
+        xg = oracle.bf16_to_f64(g["x"])
+        t = clock(lambda: oracle.gemm(xg, oracle.decode(e, cc, 8, 2048, 2048)))
+        nb = e.nbytes + cc.nbytes + 2048 * 2 + 2048 * 4
+        out["BFP8 GEMV 2048x2048 M=1"] = {"us_per_call": round(t * 1e6), "GB/s": round(nb / t / 1e9, 4),
+                                          "sample": "whole call"}
+        # LM head at M = 1: the first 16,384 of 151,936 rows
+        rows = 16384
+        wl = synth.dense_weights(0, 3, "lm", 151936, 2048, 0.02)[:rows]
+        (e, cc) = oracle.encode(wl, 8)
+        xl = oracle.bf16_to_f64(synth.proj_case(1, 0, with_lm=False)["x"])
+        t = clock(lambda: oracle.gemm(xl, oracle.decode(e, cc, 8, rows, 2048)))
+        nb = e.nbytes + cc.nbytes + rows * 4
+        out["BFP8 LM head 2048->151936 M=1"] = {"us_per_call_full": round(t * 1e6 * 151936 / rows),
+                                                "GB/s": round(nb / t / 1e9, 4),
+                                                "sample": f"rows 0..{rows} of 151936, time scaled to all rows"}
+        del wl
+        # MoE decode at M = 1 (router, top-8, 8 experts + shared), whole; and a 256-token
+        # sample of the 2,048-token prefill chunk with the skewed router bias
+        layer = synth.moe_layer(0)
+        xm = synth.moe_tokens(1, 0)
+        rt = oracle.route(xm, layer["router"], 8, sh_gate_bits=layer["sh_gate_w"])
+        bank = _PackedBank(layer, [-1] + sorted(set(rt["ids"].ravel().tolist())))
+
+        def moe_dec():
+            r = oracle.route(xm, layer["router"], 8, sh_gate_bits=layer["sh_gate_w"])
+            oracle.moe_decode(bank, xm, r)
+        t = clock(moe_dec)
+        nb = bank.nbytes + layer["router"].nbytes + layer["sh_gate_w"].nbytes + 2048 * 6
+        out["moe decode M=1"] = {"us_per_call": round(t * 1e6), "GB/s": round(nb / t / 1e9, 4), "sample": "whole call"}
+        bias = synth.router_bias(0)
+        tok = 256
+        xp = synth.moe_tokens(2048, 0, cfg_id=5)[:tok]
+        rt = oracle.route(xp, layer["router"], 8, bias=bias, sh_gate_bits=layer["sh_gate_w"])
+        bank = _PackedBank(layer, [-1] + sorted(set(rt["ids"].ravel().tolist())))
+
+        def moe_pf():
+            r = oracle.route(xp, layer["router"], 8, bias=bias, sh_gate_bits=layer["sh_gate_w"])
+            oracle.moe_prefill(bank, xp, r)
+        t = clock(moe_pf)
+        flops = 2.0 * (tok * 8 + tok) * 3 * 2048 * 512
+        out["moe prefill M=2048"] = {"tok_per_s": round(tok / t, 1), "TFLOP/s": round(flops / t / 1e12, 5),
+                                     "sample": f"tokens 0..{tok} of the 2,048-token chunk ({len(bank.packed) - 1} "
+                                               f"experts used), router bias applied"}
+        del layer, bank
+    head = out["dense BFP4 MLP M=1"]
+    return {"value": head["GB/s"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "value_1_thread": head["GB/s_1_thread"],
+            "sample": (f"dense BFP4 MLP step at M=1, whole: decode the packed BFP4 bytes (oracle encoding made "
+                       f"before timing) + fp64 GEMVs + SwiGLU + bf16 rounding, {wbytes / 1e6:.1f} MB of packed "
+                       f"weights in {dt:.2f} s on {threads} BLAS threads ({dt1:.2f} s on 1); per_config has "
+                       f"one oracle call per other workload"),
+            "per_config": out}
 
 
 # ---- other workloads -----------------------------------------------------------------------
@@ -566,7 +677,7 @@ def main():
         r = run_mlp(args, 1, mats, synth.mlp_case(1, 0)["x"], batch_invariant=True)
         workloads["dense BFP4 MLP M=1 batch-invariant"] = {k: round(v, 2) for k, v in r.items()}
         log(f"MLP M=1 batch-invariant: {r['us_per_call']:.2f} us")
-    cpu = None if args.no_cpu_baseline else cpu_baseline(c, args.cpu_rows, xb)
+    cpu = None if args.no_cpu_baseline or args.M != 1 else cpu_baseline(c, xb)
     del mats, c
     torch.cuda.empty_cache()
     if not args.quick:

@@ -75,7 +75,7 @@ _SIGS = {
     "bfp_exp_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
     "bfp_code_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]),
     "bfp_quantize": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
-                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "bfp_dequantize": (ctypes.c_int32, [ctypes.POINTER(_Tensor), ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]),
     "bfp_gemm_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor),
@@ -181,13 +181,15 @@ def empty_matrix(fmt: int, n: int, k: int, device="cuda") -> BfpMatrix:
 
 
 def bfp_quantize(fmt: int, w: torch.Tensor, out: BfpMatrix | None = None, stream=None) -> BfpMatrix:
-    """Encode a device fp32 [n][k] matrix (synchronizes the stream)."""
-    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
-        raise ValueError("w must be a contiguous fp32 [n][k] device tensor")
+    """Encode a device fp32 [n][k] matrix whose rows are contiguous (any row stride; the
+    call synchronizes the stream)."""
+    if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a row-major fp32 [n][k] device tensor")
     n, k = w.shape
     if out is None:
         out = empty_matrix(fmt, n, k, w.device)
-    _check("bfp_quantize", lib().bfp_quantize(fmt, _ptr(w), n, k, _ptr(out.exp), _ptr(out.code), _stream(stream)))
+    _check("bfp_quantize", lib().bfp_quantize(fmt, _ptr(w), n, k, w.stride(0), _ptr(out.exp), _ptr(out.code),
+                                              _stream(stream)))
     return out
 
 

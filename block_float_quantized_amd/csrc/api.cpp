@@ -22,7 +22,7 @@ int32_t check_tensor(const bfp_tensor* t) {
   if (!t) return BFP_E_ARG;
   if (!valid_fmt(t->fmt)) return BFP_E_ARG;
   if (t->n <= 0 || t->k <= 0 || (t->k % 16) != 0) return BFP_E_SHAPE;
-  if (t->n > (int64_t)1 << 31 || t->k > (int64_t)1 << 24) return BFP_E_SHAPE;
+  if (t->n > INT32_MAX || t->k > (int64_t)1 << 24) return BFP_E_SHAPE;   // kernels index rows with int
   if (!t->exp || !t->code) return BFP_E_ARG;
   if (!aligned16(t->code)) return BFP_E_ALIGN;
   return BFP_OK;
@@ -78,17 +78,17 @@ size_t bfp_code_bytes(int32_t fmt, int64_t n, int64_t k) {
   return 0;
 }
 
-int32_t bfp_quantize(int32_t fmt, const float* w, int64_t n, int64_t k, uint8_t* exp,
+int32_t bfp_quantize(int32_t fmt, const float* w, int64_t n, int64_t k, int64_t ldw, uint8_t* exp,
                      uint8_t* code, void* stream) {
   if (!valid_fmt(fmt)) return BFP_E_ARG;
   if (!w || !exp || !code) return BFP_E_ARG;
-  if (n <= 0 || k <= 0 || (k % 16) != 0) return BFP_E_SHAPE;
-  if (!aligned16(w) || !aligned16(code)) return BFP_E_ALIGN;
+  if (n <= 0 || k <= 0 || (k % 16) != 0 || ldw < k) return BFP_E_SHAPE;
+  if (!aligned16(w) || !aligned16(code) || (ldw % 4) != 0) return BFP_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int* flag = quantize_flag();
   if (!flag) return BFP_E_DEVICE;
   if (hipMemsetAsync(flag, 0, sizeof(int), s) != hipSuccess) return BFP_E_DEVICE;
-  if (bfp::quantize_launch(fmt, w, n, k, exp, code, flag, s) != hipSuccess) return BFP_E_DEVICE;
+  if (bfp::quantize_launch(fmt, w, n, k, ldw, exp, code, flag, s) != hipSuccess) return BFP_E_DEVICE;
   int h = 0;
   if (hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return BFP_E_DEVICE;
   if (hipStreamSynchronize(s) != hipSuccess) return BFP_E_DEVICE;

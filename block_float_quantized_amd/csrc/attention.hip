@@ -205,10 +205,10 @@ __device__ __forceinline__ Row8 load_row8_b4(const uint8_t* exp, const uint8_t* 
   return r;
 }
 __device__ __forceinline__ void decode_row8_b4(const Row8& r, float (&w)[8]) {
-  const float sc = block_scale<4>(r.e);
+  const int sh = block_shift<4>(r.e);
   unpack8_bfp4(r.c.x, w);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] *= sc;
+  for (int i = 0; i < 8; ++i) w[i] = apply_shift(w[i], sh);
 }
 
 struct ChunkArgs {
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kAttnThreads, V4R ? 3 : 2) void attn_chunk_mfma_ker
     for (int u = 0; u < 4; ++u) {
       const uint32_t cw[4] = {vc[u].c.x, vc[u].c.y, vc[u].c.z, vc[u].c.w};
       if constexpr (V4R) {
-        const float sc = block_scale<4>(vc[u].e);
+        const int sh = block_shift<4>(vc[u].e);
         if constexpr (DPC >= 8) {
 #pragma unroll
           for (int b = 0; b < DPC / 8; ++b) unpack8_bfp4(cw[b], vv[u] + 8 * b);
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kAttnThreads, V4R ? 3 : 2) void attn_chunk_mfma_ker
           for (int e = 0; e < 4; ++e) vv[u][e] = t8[e];
         }
 #pragma unroll
-        for (int e = 0; e < DPC; ++e) vv[u][e] *= sc;
+        for (int e = 0; e < DPC; ++e) vv[u][e] = apply_shift(vv[u][e], sh);
       } else {
         const float sc = block_scale<8>(vc[u].e);
 #pragma unroll

@@ -101,10 +101,20 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
 }
 
-// Multiplier applied to a block's unpacked integers: 2^(E - kScaleBias). Exact for every
-// E (ldexp produces the fp32 subnormal when the result is below 2^-126).
+// log2 of the multiplier of a block's unpacked integers: E - kScaleBias. Applied with
+// v_ldexp_f32 (apply_shift), which is exact for every E: a multiplier 2^(E - kScaleBias)
+// held as a float would overflow for BFP4 blocks with E >= 248 (largest |w| >= 2^121).
+template <int FMT>
+__device__ __forceinline__ int block_shift(uint32_t e) { return (int)e - FmtTraits<FMT>::kScaleBias; }
+__device__ __forceinline__ float apply_shift(float v, int sh) { return __builtin_amdgcn_ldexpf(v, sh); }
+// Shift that turns any finite value into a signed zero (masks out a clamped, duplicate unit).
+constexpr int kShiftToZero = -512;
+
+// The multiplier itself, for BFP8 only: 2^(E - 133) lies in [2^-133, 2^121], always finite
+// (ldexp gives the fp32 subnormal below 2^-126).
 template <int FMT>
 __device__ __forceinline__ float block_scale(uint32_t e) {
+  static_assert(FMT == 8, "a BFP4 multiplier overflows for E >= 248: use block_shift");
   return __builtin_amdgcn_ldexpf(1.0f, (int)e - FmtTraits<FMT>::kScaleBias);
 }
 

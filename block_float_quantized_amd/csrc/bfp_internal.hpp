@@ -7,9 +7,9 @@
 
 namespace bfp {
 
-// Encode fp32 [n][k] into exponent and code planes; `flag` is a device int set to 1 when a
-// non-finite value is met (the caller clears it before and reads it after).
-hipError_t quantize_launch(int fmt, const float* w, int64_t n, int64_t k, uint8_t* exp,
+// Encode fp32 [n][k] (row stride ldw) into exponent and code planes; `flag` is a device int
+// set to 1 when a non-finite value is met (the caller clears it before and reads it after).
+hipError_t quantize_launch(int fmt, const float* w, int64_t n, int64_t k, int64_t ldw, uint8_t* exp,
                            uint8_t* code, int* flag, hipStream_t s);
 
 // Decode a whole matrix to fp32 or bf16 [n][k].

@@ -34,6 +34,9 @@ struct PrefillArgs {
 // height the dispatch kernel must use.
 size_t prefill_workspace_extra_bytes(int m, int n_exp, int top_k, int hidden);
 int prefill_tile_rows();
+// Whether the prefill kernels take this layer and token count (tile divisibility, 32-bit byte
+// offsets); checked on the host before anything is launched.
+bool prefill_supported(const bfp_moe_layer* L, int64_t m);
 hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s);
 
 }  // namespace bfp

@@ -1,8 +1,5 @@
 // Skinny BFP4/BFP8 matmul dispatch: the matrix-core kernel (mfma_gemv.hpp) or the vector-ALU
 // kernel (gemv_impl.hpp, compiled in four translation units).
-#include <stdlib.h>
-#include <string.h>
-
 #include "bfp_internal.hpp"
 #include "mfma_gemv.hpp"
 
@@ -19,23 +16,8 @@ namespace {
 
 // One activation row runs the vector-ALU kernel (it streams the weights faster when there is
 // a single row to multiply); 2..32 rows run the matrix-core kernel. Batch-invariant calls run
-// the matrix-core kernel for every m, so that row i does not depend on m. BFP_GEMV_KERNEL=vector
-// or =mfma forces one kernel for every m in the other calls (for measurement).
-enum class Kernel { kAuto, kVector, kMfma };
-Kernel forced() {
-  static const Kernel k = [] {
-    const char* e = getenv("BFP_GEMV_KERNEL");
-    if (e && strcmp(e, "vector") == 0) return Kernel::kVector;
-    if (e && strcmp(e, "mfma") == 0) return Kernel::kMfma;
-    return Kernel::kAuto;
-  }();
-  return k;
-}
-bool use_vector(int64_t m, bool invariant) {
-  if (invariant) return false;
-  const Kernel k = forced();
-  return k == Kernel::kVector || (k == Kernel::kAuto && m == 1);
-}
+// the matrix-core kernel for every m, so that row i does not depend on m.
+bool use_vector(int64_t m, bool invariant) { return !invariant && m == 1; }
 
 hipError_t vector_launch(const GemvParams& g, hipStream_t s) {
   if (g.fmt == 4) return g.x_bf16 ? gemv_launch_b4_bf16x(g, s) : gemv_launch_b4_f32x(g, s);

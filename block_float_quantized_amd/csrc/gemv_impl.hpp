@@ -18,7 +18,7 @@
 //    pair order the weight unpack produces, and the products run on v_dot2_f32_bf16 (two
 //    products per instruction); fp32 activations use fp32 FMAs.
 //  * Weights are unpacked in registers exactly (see bfp_device.hpp); each block's partial
-//    sum is scaled once by its power-of-two block scale.
+//    sum is scaled once by its power-of-two block scale (v_ldexp_f32, exact for every E).
 //  * Partial sums are reduced across the lane group by recursive halving with DPP row moves
 //    and v_permlane16_swap; one lane per value writes y (with the SwiGLU epilogue).
 //  * Each lane's share of K and the order of its sums depend on K only, so row i of an
@@ -251,9 +251,9 @@ __device__ __forceinline__ void compute_group(float (&acc)[NMAT][RT][MB], const 
       for (int t = 0; t < NMAT; ++t)
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-          const float sc = (g.uok[u] && rowok[r]) ? block_scale<FMT>((g.e[u][t][r] >> (8 * j)) & 0xffu) : 0.f;
+          const int sh = (g.uok[u] && rowok[r]) ? block_shift<FMT>((g.e[u][t][r] >> (8 * j)) & 0xffu) : kShiftToZero;
 #pragma unroll
-          for (int i = 0; i < MB; ++i) acc[t][r][i] = __builtin_fmaf(part[j][t][r][i], sc, acc[t][r][i]);
+          for (int i = 0; i < MB; ++i) acc[t][r][i] += apply_shift(part[j][t][r][i], sh);
         }
   }
 }

@@ -152,7 +152,8 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
   if (m < 1 || m > BFP_MOE_MAX_M) return BFP_E_SHAPE;
   // many-token path: 256-column down tiles over hidden, 128-column gate/up tiles and 128-value
   // K steps over inter
-  if (m > BFP_GEMM_MAX_M && (L->hidden % 256 != 0 || L->inter % 128 != 0)) return BFP_E_UNSUPPORTED;
+  if (m > BFP_GEMM_MAX_M && (L->hidden % 256 != 0 || L->inter % 128 != 0 || !bfp::prefill_supported(L, m)))
+    return BFP_E_UNSUPPORTED;
   if (!x || !y) return BFP_E_ARG;
   if (!aligned16(x) || !aligned16(y)) return BFP_E_ALIGN;
   const Layout ly = layout(L, m, true);

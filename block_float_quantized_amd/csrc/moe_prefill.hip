@@ -549,15 +549,21 @@ static size_t items_offset(int n_exp) { return round256((size_t)(n_exp + 2) * 4)
 static size_t max_items(int m, int n_exp, int top_k) { return (size_t)(m * top_k + m) / kTM + n_exp + 1; }
 static size_t xp_offset(int m, int n_exp, int top_k) { return items_offset(n_exp) + round256(max_items(m, n_exp, top_k) * 4); }
 
+bool prefill_supported(const bfp_moe_layer* L, int64_t m) {
+  const int64_t H = L->hidden, F = L->inter, K = L->top_k;
+  // K steps come in weight blocks of two; the last column tile may be partial
+  if (H % (kTK * kBBlk) != 0 || F % (kTK * kBBlk) != 0 || F % 8 != 0) return false;
+  // activations and one expert's weights are addressed with 32-bit byte offsets
+  if (F * H / 2 >= (1ll << 31)) return false;
+  if (m * H * 2 >= (1ll << 31) || (m * K + m) * F * 2 >= (1ll << 31)) return false;
+  return true;
+}
+
 hipError_t prefill_launch(const PrefillArgs& p, hipStream_t s) {
   const bfp_moe_layer* L = p.L;
   const int shared = L->sh_gate.fmt != 0;
   const int H = (int)L->hidden, F = (int)L->inter, K = L->top_k;
-  // K steps come in weight blocks of two; the last column tile may be partial
-  if (H % (kTK * kBBlk) != 0 || F % (kTK * kBBlk) != 0 || F % 8 != 0) return hipErrorNotSupported;
-  // activations and one expert's weights are addressed with 32-bit byte offsets
-  if ((int64_t)F * H / 2 >= (1ll << 31)) return hipErrorNotSupported;
-  if ((int64_t)p.m * H * 2 >= (1ll << 31) || ((int64_t)p.m * K + p.m) * F * 2 >= (1ll << 31)) return hipErrorNotSupported;
+  if (!prefill_supported(L, p.m)) return hipErrorNotSupported;
   const int32_t* tile_start = p.extra;
   char* extra = reinterpret_cast<char*>(p.extra);
   int32_t* items = reinterpret_cast<int32_t*>(extra + items_offset(L->n_experts));

@@ -22,7 +22,8 @@
 //     for the bound below, plus the rounding of that fp64 addition). Every
 //     product of two bf16 values is exact in fp32, so |L~ - L| <= gamma * sum_k |x_k w_k| with
 //     gamma = n u / (1 - n u), n = hidden, u = 2^-23 (any summation order, any rounding that is
-//     at least truncation), plus 2^-126 (|x|_1 + |w|_1) for products flushed as subnormals;
+//     at least truncation), plus 2^-126 (|x|_1 + |w|_1) for subnormal bf16 inputs flushed to
+//     zero and n 2^-126 for products of normal inputs that underflow and are flushed;
 //     sum_k |x_k w_k| <= |x|_2 |w|_2 (Cauchy-Schwarz). This gives an interval per logit.
 //  2. per token, L_k = the k-th largest lower end. An expert whose upper end is below L_k is
 //     beaten by k experts and cannot be selected, so the top-k is among the candidates
@@ -130,29 +131,34 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
   constexpr int kPer = 4;                                   // n_exp <= 256
   double v[kPer];
   int ix[kPer];
+  bool live[kPer];                                          // not selected yet
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     ix[q] = lane + 64 * q;
-    v[q] = ix[q] < a.n_exp ? l[ix[q]] : -__builtin_huge_val();
+    live[q] = ix[q] < a.n_exp;
+    const double lv = live[q] ? l[ix[q]] : -__builtin_huge_val();
+    v[q] = lv != lv ? -__builtin_huge_val() : lv;         // a NaN logit ranks below every number
   }
   double sel_l[8];
   int sel_e[8];
   for (int j = 0; j < a.top_k; ++j) {
     // the largest remaining logit M (a max-reduction: exact, order-free), then the smallest
-    // expert index holding it: expert 64 q + lane, so the first q with a match, then its lowest
-    // lane (equality ballots, no divergent branch)
+    // unselected expert index holding it: expert 64 q + lane, so the first q with a match, then
+    // its lowest lane (equality ballots, no divergent branch). M is never NaN and at least
+    // n_exp - j >= 1 experts are live, so a match always exists: the ids are distinct and in
+    // range whatever the logits hold.
     const double M = wave_max_f64(fmax(fmax(v[0], v[1]), fmax(v[2], v[3])));
     int bi = -1;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      const uint64_t b = __ballot(ix[q] < a.n_exp && v[q] == M);
+      const uint64_t b = __ballot(live[q] && v[q] == M);
       if (bi < 0 && b != 0) bi = 64 * q + __builtin_ctzll(b);
     }
     sel_l[j] = M;
     sel_e[j] = bi;
 #pragma unroll
     for (int q = 0; q < kPer; ++q)
-      if (ix[q] == bi) v[q] = -__builtin_huge_val();
+      if (ix[q] == bi) { v[q] = -__builtin_huge_val(); live[q] = false; }
   }
   // lane j < top_k: exp(l_j - l_0) in fp64; the sum is taken in rank order (a fixed order)
   double ex = 0.0;
@@ -640,10 +646,15 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
       const double nw = sqrt(nw2) * (1.0 + 1e-12);
       // fp32 sums inside the slices: gamma |x| |w| (any summation order); the slices are added
       // in fp64 (1e-15 of their magnitudes covers that rounding)
-      const double d = gamma * nx * nw + tiny * sqrt(n) * (nx + nw) * 1.01 + 1e-15 * av;
+      // + n 2^-126: products of two normal bf16 values that fall below the fp32 normal range
+      // (each off by less than 2^-126 if the matrix cores flush them)
+      const double d = gamma * nx * nw + tiny * sqrt(n) * (nx + nw) * 1.01 + n * tiny + 1e-15 * av;
       const double b = a.bias ? (double)a.bias[e] : 0.0;
-      lo[q] = v + b - d;
-      hi[q] = v + b + d;
+      // non-finite inputs: an unknown lower end is -inf and an unknown upper end +inf, so
+      // such an expert stays a candidate and at least top_k candidates always exist
+      const double l0 = v + b - d, h0 = v + b + d;
+      lo[q] = l0 != l0 ? -__builtin_huge_val() : l0;
+      hi[q] = h0 != h0 ? __builtin_huge_val() : h0;
     } else {
       lo[q] = -__builtin_huge_val();
       hi[q] = -__builtin_huge_val();
@@ -709,7 +720,8 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
   for (int q = 0; q < 4; ++q) {
     const int i = lane + 64 * q;
     ix[q] = i < nc ? cand[wv][i] : 0x7fffffff;
-    v[q] = i < nc ? cval[wv][i] : -__builtin_huge_val();
+    const double cv = i < nc ? cval[wv][i] : -__builtin_huge_val();
+    v[q] = cv != cv ? -__builtin_huge_val() : cv;         // a NaN logit ranks below every number
   }
   double sel_l[8];
   int sel_e[8];

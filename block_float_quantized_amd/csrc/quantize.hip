@@ -9,13 +9,14 @@ namespace bfp {
 
 namespace {
 
+// Block b is block b % nbk of row b / nbk; rows of w are ldw values apart.
 template <int FMT>
-__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, int64_t nblocks,
-                                                       uint8_t* __restrict__ exp,
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, int64_t nblocks, int64_t nbk,
+                                                       int64_t ldw, uint8_t* __restrict__ exp,
                                                        uint8_t* __restrict__ code, int* flag) {
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nblocks) return;
-  const u32x4* src = reinterpret_cast<const u32x4*>(w + b * kBlock);
+  const u32x4* src = reinterpret_cast<const u32x4*>(w + (b / nbk) * ldw + (b % nbk) * kBlock);
   uint32_t u[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
                                                       int64_t nblocks, int out_bf16, void* out) {
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nblocks) return;
-  const float sc = block_scale<FMT>(exp[b]);
+  const int sh = block_shift<FMT>(exp[b]);
   float v[16];
   if constexpr (FMT == 4) {
     const uint2 c = reinterpret_cast<const uint2*>(code)[b];
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     unpack4_bfp8(c.w, v + 12);
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] *= sc;
+  for (int i = 0; i < 16; ++i) v[i] = apply_shift(v[i], sh);
   if (out_bf16) {
     // every decoded value is bf16-representable, so dropping the low half is exact
     uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + b * kBlock);
@@ -66,15 +67,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 }  // namespace
 
-hipError_t quantize_launch(int fmt, const float* w, int64_t n, int64_t k, uint8_t* exp,
+hipError_t quantize_launch(int fmt, const float* w, int64_t n, int64_t k, int64_t ldw, uint8_t* exp,
                            uint8_t* code, int* flag, hipStream_t s) {
-  const int64_t nb = n * (k / kBlock);
+  const int64_t nbk = k / kBlock;
+  const int64_t nb = n * nbk;
   if (nb == 0) return hipSuccess;
   const int64_t grid = (nb + 255) / 256;
   if (fmt == 8)
-    hipLaunchKernelGGL(quantize_kernel<8>, dim3((unsigned)grid), dim3(256), 0, s, w, nb, exp, code, flag);
+    hipLaunchKernelGGL(quantize_kernel<8>, dim3((unsigned)grid), dim3(256), 0, s, w, nb, nbk, ldw, exp, code, flag);
   else
-    hipLaunchKernelGGL(quantize_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s, w, nb, exp, code, flag);
+    hipLaunchKernelGGL(quantize_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s, w, nb, nbk, ldw, exp, code, flag);
   return hipGetLastError();
 }
 

@@ -100,18 +100,25 @@ size_t bfp_exp_bytes(int64_t n, int64_t k);
 size_t bfp_code_bytes(int32_t fmt, int64_t n, int64_t k);
 
 /*
- * Encode (round to nearest, ties to even; see Format). w: device fp32 [n][k], row stride k.
- * exp, code: device outputs sized by bfp_exp_bytes / bfp_code_bytes. Bit-exact: the same
+ * Encode (round to nearest, ties to even; see Format). w: device fp32 [n][ldw], the first k
+ * values of each row are encoded (ldw >= k, ldw a multiple of 4 so that rows stay 16-byte
+ * aligned; else BFP_E_SHAPE / BFP_E_ALIGN). exp, code: device outputs sized by bfp_exp_bytes /
+ * bfp_code_bytes, written densely ([n][k/16] and [n][k] or [n][k/2]). Bit-exact: the same
  * input gives the same bytes on every run and device ("Qwen3.6-35B-A3B ...",
- * "Verification": the round-to-nearest conversion is bit-exact). Synchronizes `stream`;
- * returns BFP_E_NONFINITE if any input value is Inf or NaN.
+ * "Verification": the round-to-nearest conversion is bit-exact; "Qwen3.8-27B ...",
+ * gptq-ctx2-20261002, "What changed in this release": values already representable
+ * re-encode bit for bit). Synchronizes `stream`; returns BFP_E_NONFINITE if any input value
+ * is Inf or NaN.
  */
-int32_t bfp_quantize(int32_t fmt, const float *w, int64_t n, int64_t k,
+int32_t bfp_quantize(int32_t fmt, const float *w, int64_t n, int64_t k, int64_t ldw,
                      uint8_t *exp, uint8_t *code, void *stream);
 
 /*
  * Decode a whole matrix: out[n][k] = (-1)^sign * mag * 2^s, exact, in fp32
- * (out_dtype = BFP_DT_F32) or bf16 (BFP_DT_BF16; every BFP value is bf16-representable).
+ * (out_dtype = BFP_DT_F32) or bf16 (BFP_DT_BF16; every BFP value is bf16-representable),
+ * for every shared exponent E. The inverse of bfp_quantize on the values it represents
+ * ("Qwen3.6-35B-A3B ...", "Verification": BFP tensors re-derived on the CPU and compared bit
+ * for bit). out: device [n][k], 16-byte aligned.
  */
 int32_t bfp_dequantize(const bfp_tensor *w, int32_t out_dtype, void *out, void *stream);
 
@@ -123,7 +130,11 @@ int32_t bfp_dequantize(const bfp_tensor *w, int32_t out_dtype, void *out, void *
 size_t bfp_gemm_workspace_bytes(const bfp_tensor *w, const bfp_tensor *w_up, int64_t m);
 
 /*
- * Skinny matmul over streamed BFP weights, dequantized in registers:
+ * Skinny matmul over streamed BFP weights, dequantized in registers ("Qwen3.6-35B-A3B ...",
+ * "Precision as served": dense projections and LM head in BFP8, experts in BFP4; "Speed":
+ * decode cost follows the weight bytes read; "Qwen3.8-27B ...", "What changed in this
+ * release (s27v6-20261024)" and "Multi-user decode": up to 32 rows share one pass over every
+ * weight, the MLP being gate/up with SwiGLU then down):
  *   epilogue NONE  : y[i][j] = sum_k x[i][k] * W[j][k]
  *   epilogue SWIGLU: y[i][j] = silu(sum_k x[i][k] * W[j][k]) * (sum_k x[i][k] * Wup[j][k])
  * with silu(g) = g / (1 + e^-g). i < m (1..BFP_GEMM_MAX_M rows share one pass over the
@@ -195,7 +206,9 @@ typedef struct bfp_moe_layer {
 size_t bfp_moe_route_workspace_bytes(const bfp_moe_layer *L, int64_t m);
 
 /*
- * Routing step of bfp_moe_forward, exposed on its own. For each token t < m:
+ * Routing step of bfp_moe_forward, exposed on its own ("Qwen3.6-35B-A3B ...", "Precision as
+ * served": BF16 router; "Fused decode kernels": device top-k routing; "qwen3.6-a3b-blackhole",
+ * introduction: 256 experts, top-8, a shared expert). For each token t < m:
  *   l_e = sum_k x[t][k] * router_w[e][k] (+ router_bias[e]), exact bf16 products summed
  *         in fp64;
  *   ids[t][0..top_k) = the top_k experts by (l descending, e ascending), in that order;
@@ -205,14 +218,17 @@ size_t bfp_moe_route_workspace_bytes(const bfp_moe_layer *L, int64_t m);
  * x: device bf16 [m][hidden]; ids: device int32 [m][top_k]; w: device fp32 [m][top_k];
  * g: device fp32 [m] or NULL; ws: device workspace of at least
  * bfp_moe_route_workspace_bytes(L, m) bytes. Only the router fields of L are read.
- * m > BFP_GEMM_MAX_M needs hidden % 64 == 0 (else BFP_E_UNSUPPORTED). Inputs must be finite
- * (a token whose logits hold Inf or NaN gets an unspecified selection).
+ * m > BFP_GEMM_MAX_M needs hidden % 64 == 0 (else BFP_E_UNSUPPORTED). Non-finite inputs:
+ * a NaN logit ranks below every number, so ids always hold top_k distinct experts in
+ * [0, n_experts) in the rule's order; the weights of such a token are unspecified.
  */
 int32_t bfp_moe_route(const bfp_moe_layer *L, const uint16_t *x, int64_t m,
                       int32_t *ids, float *w, float *g, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Dispatch structure for expert-grouped execution (counting sort by expert):
+ * Dispatch structure for expert-grouped execution (counting sort by expert), the grouping of
+ * "batched expert streams" ("Qwen3.6-35B-A3B ...", "Fused decode kernels") and of a
+ * 2,048-token prefill chunk run expert by expert ("Qwen3.8-27B ...", s27v6 bullets):
  *   counts[e]  = number of (token, slot) pairs routed to expert e;
  *   offsets[e] = sum of counts below e (n_experts + 1 entries, offsets[n_experts] = m*top_k);
  *   perm[p]    = pair ids top_k*t + j ordered by (expert ascending, token ascending).

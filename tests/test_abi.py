@@ -47,11 +47,13 @@ def _tensor(fmt=4, n=32, k=64, exp=16, code=16):
 def test_host_validation_before_any_launch():
     lib = bfq.lib()
     # quantize
-    assert lib.bfp_quantize(5, 16, 4, 16, 16, 16, None) == 1          # unknown format
-    assert lib.bfp_quantize(4, None, 4, 16, 16, 16, None) == 1         # null pointer
-    assert lib.bfp_quantize(4, 16, 4, 24, 16, 16, None) == 2           # k % 16
-    assert lib.bfp_quantize(4, 16, 0, 16, 16, 16, None) == 2           # n = 0
-    assert lib.bfp_quantize(4, 18, 4, 16, 16, 16, None) == 3           # misaligned input
+    assert lib.bfp_quantize(5, 16, 4, 16, 16, 16, 16, None) == 1      # unknown format
+    assert lib.bfp_quantize(4, None, 4, 16, 16, 16, 16, None) == 1     # null pointer
+    assert lib.bfp_quantize(4, 16, 4, 24, 24, 16, 16, None) == 2       # k % 16
+    assert lib.bfp_quantize(4, 16, 0, 16, 16, 16, 16, None) == 2       # n = 0
+    assert lib.bfp_quantize(4, 16, 4, 32, 16, 16, 16, None) == 2       # row stride below k
+    assert lib.bfp_quantize(4, 18, 4, 16, 16, 16, 16, None) == 3       # misaligned input
+    assert lib.bfp_quantize(4, 16, 4, 16, 18, 16, 16, None) == 3       # row stride not 16-byte aligned
     # dequantize
     t = _tensor(k=40)
     assert lib.bfp_dequantize(ctypes.byref(t), 0, 16, None) == 2
@@ -100,6 +102,30 @@ def test_host_validation_before_any_launch():
     assert lib.bfp_gemm(ctypes.byref(w), None, 0x200, 16, 1, 1, 64, 16, 0, 32, None, 0, None) == 1
     assert lib.bfp_gemm(ctypes.byref(big), None, 0x100, 16, 1, 1, 16384, 16, 0, 64, None, 0, None) == 5
     assert lib.bfp_gemm_workspace_bytes(ctypes.byref(big), None, 1) > 0
+
+
+def _fake_layer(hidden, inter, n_exp=256, top_k=8):
+    t = lambda n, k: bfq._Tensor(4, n, k, 16, 16)
+    return bfq._MoeLayer(n_exp, top_k, hidden, inter, 16, None, t(n_exp * inter, hidden), t(n_exp * inter, hidden),
+                         t(n_exp * hidden, inter), t(inter, hidden), t(inter, hidden), t(hidden, inter), 16)
+
+
+def test_moe_host_validation():
+    """Shapes the many-token kernels cannot address with 32-bit offsets are refused on the
+    host (BFP_E_UNSUPPORTED) before the routing or dispatch kernels are queued."""
+    lib = bfq.lib()
+    L = _fake_layer(2048, 14592)          # (8192 * 8 + 8192) * 14592 * 2 B of h >= 2^31
+    assert lib.bfp_moe_forward(ctypes.byref(L), 16, 8192, 16, None, None, 16, 1 << 40, None) == 7
+    assert lib.bfp_moe_forward(ctypes.byref(L), 16, 32, 16, None, None, None, 0, None) == 5   # decode: workspace
+    L = _fake_layer(2048, 96)             # inter not a multiple of the 128-value K step
+    assert lib.bfp_moe_forward(ctypes.byref(L), 16, 64, 16, None, None, 16, 1 << 40, None) == 7
+    L = _fake_layer(2048, 512)
+    assert lib.bfp_moe_forward(ctypes.byref(L), 16, 8193, 16, None, None, 16, 1 << 40, None) == 2  # m
+    assert lib.bfp_moe_forward(ctypes.byref(L), 24, 4, 16, None, None, 16, 1 << 40, None) == 3    # x alignment
+    bad = _fake_layer(2048, 512, top_k=9)
+    assert lib.bfp_moe_forward(ctypes.byref(bad), 16, 4, 16, None, None, 16, 1 << 40, None) == 2
+    huge = bfq._Tensor(4, 1 << 31, 64, 16, 16)      # rows beyond the kernels' int range
+    assert lib.bfp_dequantize(ctypes.byref(huge), 0, 16, None) == 2
 
 
 def test_kv_cache_host_validation():

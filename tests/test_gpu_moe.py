@@ -184,14 +184,14 @@ def test_moe_prefill_multi_chunk_dispatch(moe_full, crowded):
 
 
 def test_moe_prefill_chunk_2048(moe_full):
-    """The 2,048-token prefill chunk with a skewed N(0, 1.5) per-expert router bias."""
+    """The 2,048-token prefill chunk with a skewed N(0, 1.5) per-expert router bias: every
+    output of every token."""
     layer, dev, bank = moe_full
     note("moe prefill m=2048 with bias")
     bias = synth.router_bias(0)
     devb = bfq.MoeLayer(**{**dev.__dict__, "router_bias": dev_f32(bias)})
     x = synth.moe_tokens(2048, 0, cfg_id=5)
-    sample = np.unique(np.concatenate([[0, 2047], np.random.default_rng(5).integers(0, 2048, 62)]))
-    _prefill_check(layer, devb, bank, x, bias, sample)
+    _prefill_check(layer, devb, bank, x, bias, np.arange(2048))
 
 
 def test_moe_prefill_and_decode_agree(moe_full):
@@ -205,6 +205,85 @@ def test_moe_prefill_and_decode_agree(moe_full):
     rt = oracle.route(x, layer["router"], 8, sh_gate_bits=layer["sh_gate_w"])
     _, norm = oracle.moe_decode(bank, x, rt)
     assert np.all(np.abs(yp - yd) <= 2.0 ** -7 * norm)
+
+
+def _small_layer(seed, gate_scale=1.0, x_scale=1.0, n_exp=16, hidden=256, inter=64, top_k=4):
+    """A small layer (fp32 weights, oracle-encodable) with the workload's distributions; gate and
+    up of every expert (and the shared one) scaled by gate_scale."""
+    rng = np.random.default_rng(seed)
+
+    def mat(r, c, s=1.0):
+        return (rng.standard_normal((r, c)) * 0.02 * s).astype(np.float32)
+    return {
+        "fmt": 4, "n_experts": n_exp, "top_k": top_k, "hidden": hidden, "inter": inter,
+        "router": synth.normal_bf16(rng, (n_exp, hidden), std=0.02 / x_scale),
+        "sh_gate_w": synth.normal_bf16(rng, (hidden,), std=0.02 / x_scale),
+        "gate": mat(n_exp * inter, hidden, gate_scale), "up": mat(n_exp * inter, hidden, gate_scale),
+        "down": mat(n_exp * hidden, inter),
+        "sh_gate": mat(inter, hidden, gate_scale), "sh_up": mat(inter, hidden, gate_scale),
+        "sh_down": mat(hidden, inter),
+    }
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_moe_decode_extreme_exponents(m):
+    """Gate and up weights near 2^121 (shared exponents 245..254) with activations near
+    2^-120: the decode expert kernels apply the BFP4 block scale exactly for every exponent."""
+    note(f"moe decode extreme exponents m={m}")
+    layer = _small_layer(31, gate_scale=2.0 ** 123, x_scale=2.0 ** -120)
+    e, _ = oracle.encode(layer["gate"], 4)
+    assert e.max() >= 248
+    dev = device_layer(layer)
+    rng = np.random.default_rng(32)
+    x = synth.bf16_bits((rng.standard_normal((m, layer["hidden"])) * 2.0 ** -120).astype(np.float32))
+    ids = torch.empty((m, layer["top_k"]), dtype=torch.int32, device="cuda")
+    y = bfq.bfp_moe_forward(dev, dev_bf16(x), topk_ids=ids).cpu().numpy()
+    rt = oracle.route(x, layer["router"], layer["top_k"], sh_gate_bits=layer["sh_gate_w"])
+    assert np.array_equal(ids.cpu().numpy(), rt["ids"])
+    ref, norm = oracle.moe_decode(LazyBank(layer), x, rt)
+    assert np.all(np.isfinite(y))
+    assert_within(y, ref, norm, TOL, what="moe decode extreme exponents")
+
+
+@pytest.mark.parametrize("m", [4, 40])
+def test_route_nan_token(m):
+    """A token whose activations hold NaN (so every logit is NaN) still gets top-k distinct
+    experts in range: NaN ranks below every number, ties go to the lower index, so it takes
+    experts 0..7. The other tokens route as the oracle does (decode path at m = 4, the
+    certified many-token path at m = 40)."""
+    note(f"route NaN token m={m}")
+    lay, router, shg = _router_only_layer(0)
+    x = synth.moe_tokens(m, 2)
+    bad = 1
+    x[bad, 7] = 0x7FC0                      # bf16 quiet NaN
+    ids, w, g = bfq.bfp_moe_route(lay, dev_bf16(x))
+    ids = ids.cpu().numpy()
+    assert ids[bad].tolist() == list(range(8))
+    ok = np.array([t for t in range(m) if t != bad])
+    ref = oracle.route(x[ok], router, 8, sh_gate_bits=shg)
+    assert np.array_equal(ids[ok], ref["ids"])
+    assert np.allclose(w.cpu().numpy()[ok], ref["r"], rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("m", [4, 40])
+def test_moe_forward_nan_token(moe_full, m):
+    """A NaN token through the whole layer (decode at m = 4, prefill at m = 40): its expert
+    ids stay valid, so the dispatch and the expert kernels read only real rows, and every other
+    token's output matches the oracle."""
+    layer, dev, bank = moe_full
+    note(f"moe forward NaN token m={m}")
+    x = synth.moe_tokens(m, 6)
+    bad = m - 2
+    x[bad, 100] = 0x7FC0
+    ids = torch.empty((m, 8), dtype=torch.int32, device="cuda")
+    y = bfq.bfp_moe_forward(dev, dev_bf16(x), topk_ids=ids).cpu().numpy()
+    assert ids.cpu().numpy()[bad].tolist() == list(range(8))
+    ok = np.array([t for t in range(m) if t != bad])
+    rt = oracle.route(x[ok], layer["router"], 8, sh_gate_bits=layer["sh_gate_w"])
+    assert np.array_equal(ids.cpu().numpy()[ok], rt["ids"])
+    fn = oracle.moe_decode if m <= 32 else oracle.moe_prefill
+    ref, norm = fn(bank, x[ok], rt)
+    assert_within(y[ok], ref, norm, TOL, what=f"moe forward with a NaN token m={m}")
 
 
 def test_route_many_tokens_with_exact_ties():
