@@ -22,7 +22,8 @@ __all__ = [
     "bfp_quantize", "bfp_dequantize", "bfp_gemm", "bfp_gemm_workspace_bytes", "bfp_gemm_argmax",
     "bfp_gemm_argmax_workspace_bytes", "bfp_moe_route", "bfp_moe_dispatch", "KvCache", "KV_V_BFP8", "KV_V_BFP4_HADAMARD", "bfp_kv_append",
     "bfp_attn_decode", "bfp_attn_decode_workspace_bytes",
-    "bfp_moe_workspace_bytes", "bfp_moe_forward", "exp_bytes", "code_bytes",
+    "bfp_moe_workspace_bytes", "bfp_moe_forward", "bfp_moe_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES",
+    "exp_bytes", "code_bytes",
 ]
 
 BFP4 = 4
@@ -104,6 +105,9 @@ _SIGS = {
     "bfp_moe_forward": (ctypes.c_int32, [ctypes.POINTER(_MoeLayer), ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]),
+    "bfp_moe_forward_noalloc": (ctypes.c_int32, [ctypes.POINTER(_MoeLayer), ctypes.c_void_p, ctypes.c_int64,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p]),
 }
 
 
@@ -407,4 +411,18 @@ def bfp_moe_forward(layer: MoeLayer, x: torch.Tensor, out: torch.Tensor | None =
     st = lib().bfp_moe_forward(ctypes.byref(v), _ptr(x), m, _ptr(out), _ptr(topk_ids), _ptr(topk_w),
                                _ptr(workspace), workspace.numel(), _stream(stream))
     _check("bfp_moe_forward", st)
+    return out
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def bfp_moe_forward_noalloc(layer: MoeLayer, x: torch.Tensor, out: torch.Tensor, topk_ids: torch.Tensor | None = None,
+                            topk_w: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode MoE (m <= 32) on the library's own device scratch: allocates nothing (the caller
+    passes the output). Calls that overlap on one device race."""
+    v = layer.view()
+    st = lib().bfp_moe_forward_noalloc(ctypes.byref(v), _ptr(x), x.shape[0], _ptr(out), _ptr(topk_ids),
+                                       _ptr(topk_w), _stream(stream))
+    _check("bfp_moe_forward_noalloc", st)
     return out

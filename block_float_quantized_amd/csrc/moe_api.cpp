@@ -2,6 +2,9 @@
 // (router logits -> top-k + dispatch -> grouped gate/up + SwiGLU -> grouped down -> combine).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/libbfp.h"
 #include "bfp_moe.hpp"
 #include "bfp_prefill.hpp"
@@ -145,8 +148,12 @@ size_t bfp_moe_workspace_bytes(const bfp_moe_layer* L, int64_t m) {
   return layout(L, m, true).total;
 }
 
-int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, float* y, int32_t* topk_ids,
-                        float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks of bfp_moe_forward that do not involve the workspace.
+int32_t check_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, const float* y) {
   int32_t st = check_layer(L);
   if (st != BFP_OK) return st;
   if (m < 1 || m > BFP_MOE_MAX_M) return BFP_E_SHAPE;
@@ -156,10 +163,13 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
     return BFP_E_UNSUPPORTED;
   if (!x || !y) return BFP_E_ARG;
   if (!aligned16(x) || !aligned16(y)) return BFP_E_ALIGN;
+  return BFP_OK;
+}
+
+// The layer's kernels on a checked call; ws holds at least layout(L, m, true).total bytes.
+int32_t moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, float* y, int32_t* topk_ids,
+                    float* topk_w, void* ws, hipStream_t s) {
   const Layout ly = layout(L, m, true);
-  if (!ws || ws_bytes < ly.total) return BFP_E_WORKSPACE;
-  if (!aligned16(ws)) return BFP_E_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const bool shared = L->sh_gate.fmt != 0;
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, ly.ids);
   float* w = topk_w ? topk_w : at<float>(ws, ly.w);
@@ -226,6 +236,58 @@ int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, fl
   c.o = o; c.inv = d.inv; c.w = w; c.g = shared ? g : nullptr;
   c.m = (int)m; c.top_k = L->top_k; c.hidden = (int)L->hidden; c.y = y;
   return from_hip(bfp::combine_launch(c, s));
+}
+
+// Scratch of bfp_moe_forward_noalloc: the decode workspace in a file-scope device array, one
+// copy per device, held until the process ends. In host code `scratch` only names the symbol:
+// its device address comes from hipGetSymbolAddress, once per device (with that device
+// current), and only that address is handed to kernels.
+__device__ __align__(256) unsigned char scratch[BFP_MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (looked up on the first call on a device).
+int32_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BFP_E_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return BFP_E_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return BFP_E_DEVICE;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return BFP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bfp_moe_forward_noalloc(const bfp_moe_layer* L, const uint16_t* x, int64_t m, float* y,
+                                int32_t* topk_ids, float* topk_w, void* stream) {
+  int32_t st = check_forward(L, x, m, y);
+  if (st != BFP_OK) return st;
+  if (m > BFP_GEMM_MAX_M) return BFP_E_UNSUPPORTED;
+  if (layout(L, m, true).total > BFP_MOE_NOALLOC_SCRATCH_BYTES) return BFP_E_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != BFP_OK) return st;
+  return moe_forward(L, x, m, y, topk_ids, topk_w, ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t bfp_moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, float* y, int32_t* topk_ids,
+                        float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_forward(L, x, m, y);
+  if (st != BFP_OK) return st;
+  if (!ws || ws_bytes < layout(L, m, true).total) return BFP_E_WORKSPACE;
+  if (!aligned16(ws)) return BFP_E_ALIGN;
+  return moe_forward(L, x, m, y, topk_ids, topk_w, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

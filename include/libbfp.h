@@ -260,6 +260,23 @@ int32_t bfp_moe_forward(const bfp_moe_layer *L, const uint16_t *x, int64_t m, fl
                         void *stream);
 
 /*
+ * bfp_moe_forward for decode (1..BFP_GEMM_MAX_M tokens) without a caller workspace and
+ * without any allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). Same kernels and same
+ * results, bit for bit, as bfp_moe_forward with a workspace. The workspace is a scratch array
+ * of BFP_MOE_NOALLOC_SCRATCH_BYTES in the library's device code, one per device (held until
+ * the process ends; its address is looked up on the first call on a device). Every call on a
+ * device shares that device's scratch: calls that overlap on one device (other streams,
+ * other host threads) race and must be serialised by the caller. Nothing in it needs to start
+ * at zero. Errors: m > BFP_GEMM_MAX_M gives BFP_E_UNSUPPORTED; a layer whose decode
+ * workspace (bfp_moe_workspace_bytes(L, m)) exceeds BFP_MOE_NOALLOC_SCRATCH_BYTES gives
+ * BFP_E_WORKSPACE; all other arguments as bfp_moe_forward.
+ */
+#define BFP_MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int32_t bfp_moe_forward_noalloc(const bfp_moe_layer *L, const uint16_t *x, int64_t m, float *y,
+                                int32_t *topk_ids, float *topk_w, void *stream);
+
+/*
  * BFP8 KV cache for decode attention ("Qwen3.6-35B-A3B ...", "Precision as served": the KV
  * cache is BFP8; serving-settings table, KV-precision row: BFP8 halves the cache, 20.0 ->
  * 10.6 KiB per token, and decode attention, which reads the whole cache every step, gets

@@ -124,6 +124,15 @@ def test_moe_host_validation():
     assert lib.bfp_moe_forward(ctypes.byref(L), 24, 4, 16, None, None, 16, 1 << 40, None) == 3    # x alignment
     bad = _fake_layer(2048, 512, top_k=9)
     assert lib.bfp_moe_forward(ctypes.byref(bad), 16, 4, 16, None, None, 16, 1 << 40, None) == 2
+    # the no-allocation decode variant: decode sizes only, and a layer whose decode workspace
+    # fits the static scratch
+    L = _fake_layer(2048, 512)
+    assert lib.bfp_moe_forward_noalloc(ctypes.byref(L), 16, 33, 16, None, None, None) == 7
+    assert lib.bfp_moe_workspace_bytes(ctypes.byref(L), 32) <= bfq.MOE_NOALLOC_SCRATCH_BYTES
+    big = _fake_layer(8192, 512)
+    assert lib.bfp_moe_workspace_bytes(ctypes.byref(big), 32) > bfq.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.bfp_moe_forward_noalloc(ctypes.byref(big), 16, 32, 16, None, None, None) == 5
+    assert lib.bfp_moe_forward_noalloc(ctypes.byref(L), 24, 4, 16, None, None, None) == 3
     huge = bfq._Tensor(4, 1 << 31, 64, 16, 16)      # rows beyond the kernels' int range
     assert lib.bfp_dequantize(ctypes.byref(huge), 0, 16, None) == 2
 

@@ -227,15 +227,16 @@ def _small_layer(seed, gate_scale=1.0, x_scale=1.0, n_exp=16, hidden=256, inter=
 
 @pytest.mark.parametrize("m", [1, 4])
 def test_moe_decode_extreme_exponents(m):
-    """Gate and up weights near 2^121 (shared exponents 245..254) with activations near
-    2^-120: the decode expert kernels apply the BFP4 block scale exactly for every exponent."""
+    """Gate and up weights near 2^123 (shared exponents up to ~252) with activations near
+    2^-112 (products stay normal fp32 numbers): the decode expert kernels apply the BFP4 block
+    scale exactly for every exponent."""
     note(f"moe decode extreme exponents m={m}")
-    layer = _small_layer(31, gate_scale=2.0 ** 123, x_scale=2.0 ** -120)
+    layer = _small_layer(31, gate_scale=2.0 ** 128, x_scale=2.0 ** -112)
     e, _ = oracle.encode(layer["gate"], 4)
     assert e.max() >= 248
     dev = device_layer(layer)
     rng = np.random.default_rng(32)
-    x = synth.bf16_bits((rng.standard_normal((m, layer["hidden"])) * 2.0 ** -120).astype(np.float32))
+    x = synth.bf16_bits((rng.standard_normal((m, layer["hidden"])) * 2.0 ** -112).astype(np.float32))
     ids = torch.empty((m, layer["top_k"]), dtype=torch.int32, device="cuda")
     y = bfq.bfp_moe_forward(dev, dev_bf16(x), topk_ids=ids).cpu().numpy()
     rt = oracle.route(x, layer["router"], layer["top_k"], sh_gate_bits=layer["sh_gate_w"])
