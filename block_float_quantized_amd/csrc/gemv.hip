@@ -1,9 +1,30 @@
 // Skinny BFP4/BFP8 matmul dispatch: the matrix-core kernel (mfma_gemv.hpp) or the vector-ALU
 // kernel (gemv_impl.hpp, compiled in four translation units).
+#include <atomic>
+
 #include "bfp_internal.hpp"
+#include "gemv_row.hpp"
 #include "mfma_gemv.hpp"
 
 namespace bfp {
+
+namespace rowk {
+
+// Compute units per device, looked up once per device.
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+}  // namespace rowk
 
 hipError_t gemv_launch_b4_bf16x(const GemvParams& g, hipStream_t s);
 hipError_t gemv_launch_b4_f32x(const GemvParams& g, hipStream_t s);

@@ -1,9 +1,24 @@
 // Instantiates the skinny BFP8 matmul kernels for bf16 activations.
 #include "gemv_impl.hpp"
+#include "gemv_row.hpp"
 
 namespace bfp {
 
 hipError_t gemv_launch_b8_bf16x(const GemvParams& g, hipStream_t s) {
+  const bool am = g.am_idx != nullptr;
+  if (g.m == 1 && rowk::supported((int)g.n, (int)g.k, true, g.u_code != nullptr ? 2 : 1)) {
+    // one activation row: the wave-per-row kernel
+    rowk::RowArgs r{};
+    r.exp[0] = g.w_exp; r.code[0] = g.w_code;
+    r.exp[1] = g.u_exp; r.code[1] = g.u_code;
+    r.x = g.x; r.y = g.y; r.y_bf16 = g.y_bf16;
+    r.n = (int)g.n; r.k = (int)g.k;
+    r.cand = am ? static_cast<uint64_t*>(g.ws) : nullptr;
+    int grid = 0;
+    const hipError_t e = rowk::launch<8, true>(r, g.u_code != nullptr ? 2 : 1, &grid, s);
+    if (e != hipSuccess || !am) return e;
+    return am::launch_rows<false>(r.cand, nullptr, 0, grid, 1, g.am_idx, g.am_val, s);
+  }
   gemv_detail::GemvArgs a{};
   a.exp0 = g.w_exp; a.code0 = g.w_code;
   a.exp1 = g.u_exp; a.code1 = g.u_code;
@@ -11,7 +26,7 @@ hipError_t gemv_launch_b8_bf16x(const GemvParams& g, hipStream_t s) {
   a.n = (int)g.n; a.k = (int)g.k; a.m = (int)g.m;
   a.y_bf16 = g.y_bf16;
   a.kc = 0;
-  if (g.am_idx != nullptr) {
+  if (am) {
     a.cand = static_cast<uint64_t*>(g.ws);
     a.am_idx = g.am_idx;
     a.am_val = g.am_val;

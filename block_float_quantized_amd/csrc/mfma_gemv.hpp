@@ -78,35 +78,6 @@ struct StepRegs {
 
 // ---- dequantisation to bf16 pairs (8 values -> 4 dwords) -----------------------------------
 
-// BFP4, exponent in [8, 247]: 2^(E-120) is a normal fp32 and every result a normal bf16.
-__device__ __forceinline__ u32x4 dq8_bfp4_fast(uint32_t c, float sc) {
-  const uint32_t ev = ((c << 4) & 0x80808080u) | (c & 0x07070707u);
-  const uint32_t od = (c & 0x80808080u) | ((c >> 4) & 0x07070707u);
-  u32x4 o;
-  o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, false));   // (v0, v2)
-  o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, sc, true));    // (v4, v6)
-  o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, false));   // (v1, v3)
-  o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, sc, true));    // (v5, v7)
-  return o;
-}
-
-// BFP4, any exponent: fp32 values scaled by ldexp (exact, subnormals included); a value with
-// at most 3 significant bits and a multiple of 2^-133 is its own bf16, the top half of the fp32.
-__device__ __forceinline__ u32x4 dq8_bfp4_any(uint32_t c, uint32_t e) {
-  float w[8];
-  unpack8_bfp4(c, w);
-  const int sh = (int)e - FmtTraits<4>::kScaleBias;
-  uint32_t b[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) b[i] = __float_as_uint(__builtin_amdgcn_ldexpf(w[i], sh));
-  u32x4 o;
-  o.x = __builtin_amdgcn_perm(b[2], b[0], 0x07060302u);
-  o.y = __builtin_amdgcn_perm(b[6], b[4], 0x07060302u);
-  o.z = __builtin_amdgcn_perm(b[3], b[1], 0x07060302u);
-  o.w = __builtin_amdgcn_perm(b[7], b[5], 0x07060302u);
-  return o;
-}
-
 // BFP8, any exponent: |code| as fp32 times the block scale 2^(E-133) (exact: at most 7
 // significant bits, a multiple of 2^-133), sign bit copied, top halves packed. Pair order
 // (v0, v2) (v1, v3) (v4, v6) (v5, v7).

@@ -76,7 +76,7 @@ def _case(fmt, n, k, m, seed):
 # (n, k): ragged N and K; K up to one step (one K slice on the matrix cores) and longer K
 # (sliced on the matrix cores for these N)
 @pytest.mark.parametrize("fmt", [BFP8, BFP4])
-@pytest.mark.parametrize("n,k", [(1, 16), (37, 48), (777, 112), (1000, 2048), (3001, 1040)])
+@pytest.mark.parametrize("n,k", [(1, 16), (37, 48), (777, 112), (1000, 2048), (3001, 1040), (9, 1024), (2500, 5120)])
 @pytest.mark.parametrize("m", [1, 2, 5, 16, 32])
 def test_argmax_small_shapes(fmt, n, k, m):
     note(f"argmax fmt={fmt} n={n} k={k} m={m}")

@@ -48,6 +48,53 @@ def test_gemm_small_shapes(fmt, n, k, m):
     assert_within(y, oracle.gemm(x64, wd), oracle.normaliser(x64, wd), TOL, what="gemm")
 
 
+# one activation row with K a multiple of 1024 runs the wave-per-row kernel: slices of 1..5
+# steps (bf16 x) or 1..2 (fp32 x), one workgroup per compute unit, ragged row shares
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+@pytest.mark.parametrize("n,k", [(1, 1024), (7, 2048), (300, 3072), (257, 4096), (2049, 5120), (96, 6144),
+                                 (5000, 2048), (40, 17408)])
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_gemm_one_row_shapes(fmt, n, k, x_dtype):
+    note(f"gemm m=1 fmt={fmt} n={n} k={k} x={x_dtype}")
+    wm, wd, x64, xt = _case(fmt, n, k, 1, seed=n + k + fmt, x_dtype=x_dtype)
+    y = bfq.bfp_gemm(wm, xt).cpu().numpy()
+    assert_within(y, oracle.gemm(x64, wd), oracle.normaliser(x64, wd), TOL, what="gemm m=1")
+    yb = bfq.bfp_gemm(wm, xt, out_dtype=torch.bfloat16)
+    ref = oracle.gemm(x64, wd)
+    assert_within(_bf16_values(host_bits_bf16(yb)), ref, oracle.normaliser(x64, wd), TOL,
+                  extra=2.0 ** -8 * np.abs(ref), what="gemm m=1 bf16 out")
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+@pytest.mark.parametrize("n,k", [(5, 1024), (333, 5120), (1200, 3072)])
+def test_gemm_one_row_swiglu(fmt, n, k):
+    note(f"gemm m=1 swiglu fmt={fmt} n={n} k={k}")
+    wg, gd, x64, xt = _case(fmt, n, k, 1, seed=n + 3 * k + fmt)
+    rng = np.random.default_rng(n + 1)
+    wu = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    eu, cu = oracle.encode(wu, fmt)
+    ud = oracle.decode(eu, cu, fmt, n, k)
+    h = bfq.bfp_gemm(wg, xt, w_up=matrix_from_oracle(fmt, eu, cu, n, k)).cpu().numpy()
+    g, u = oracle.gemm(x64, gd), oracle.gemm(x64, ud)
+    ref = oracle.swiglu(g, u)
+    norm = 1.1 * oracle.normaliser(x64, gd) * np.abs(u) + np.abs(oracle.silu(g)) * oracle.normaliser(x64, ud)
+    assert_within(h, ref, norm, TOL, extra=1e-6 * np.abs(ref), what="swiglu m=1")
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+def test_gemm_one_row_one_hot_bit_exact(fmt):
+    """A one-hot row through the wave-per-row kernel: one exact product per output."""
+    note(f"gemm m=1 one-hot fmt={fmt}")
+    n, k = 777, 5120
+    wm, wd, _, _ = _case(fmt, n, k, 1, seed=9 + fmt)
+    for col, val in ((4099, -1.375), (0, 3.0e-3), (5119, 7.5)):
+        xb = np.zeros((1, k), np.uint16)
+        xb[0, col] = synth.bf16_bits(np.array([val], np.float32))[0]
+        y = bfq.bfp_gemm(wm, dev_bf16(xb)).cpu().numpy()
+        want = (oracle.bf16_to_f64(xb) @ wd.T).astype(np.float32)
+        assert np.array_equal(y.view(np.uint32), want.view(np.uint32)), f"column {col}"
+
+
 @pytest.mark.parametrize("fmt", [BFP8, BFP4])
 @pytest.mark.parametrize("m", [1, 5, 16])
 def test_gemm_fp32_x_and_bf16_y(fmt, m):
