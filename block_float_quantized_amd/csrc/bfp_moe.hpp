@@ -40,6 +40,8 @@ struct DispatchArgs {
 };
 size_t dispatch_scratch_bytes(int m);
 hipError_t dispatch_launch(const DispatchArgs& a, hipStream_t s);
+// Decode (m <= 32): the router logits alone (fp64, n_exp + 1 columns per token).
+hipError_t router_logits_launch(const RouteArgs& a, hipStream_t s);
 // Decode (m <= 32): the router logits, then top-k and dispatch in one single-workgroup kernel
 // (router_launch + dispatch_launch with one launch fewer; d.ids must be r.ids).
 hipError_t route_dispatch_launch(const RouteArgs& r, const DispatchArgs& d, hipStream_t s);
@@ -82,5 +84,29 @@ struct CombineArgs {
   float* y;                    // [m][hidden]
 };
 hipError_t combine_launch(const CombineArgs& a, hipStream_t s);
+
+// One token in two launches after the router logits: (1) every workgroup of the gate/up grid
+// ranks the experts itself from the logits and streams its rows of the selected expert of its
+// slot (slot top_k: the shared expert); one of them also writes ids, w and g; (2) each
+// workgroup of the down grid computes a few output columns of every slot's down projection
+// and combines them. The per-row arithmetic is that of the grouped kernels above (same tile,
+// same lane split and order), so a token's output does not depend on the batch size.
+struct Moe1Args {
+  const double* logits;                             // [n_exp + 1] (the last: shared-gate logit)
+  int n_exp, top_k;
+  int gate_row;                                     // a shared-gate logit is present
+  const uint16_t* x;                                // bf16 [hidden]
+  int hidden, inter;
+  const uint8_t *g_exp, *g_code, *u_exp, *u_code, *d_exp, *d_code;       // routed, stacked
+  const uint8_t *sg_exp, *sg_code, *su_exp, *su_code, *sd_exp, *sd_code; // shared (null: none)
+  int32_t* ids;                                     // [top_k], rank order
+  float* w;                                         // [top_k]
+  float* g;                                         // [1] (written when there is a shared expert)
+  float* h;                                         // fp32 [top_k + 1][inter], row = slot
+  float* y;                                         // fp32 [hidden]
+};
+// Whether the one-token kernels take this layer (the down kernel stages every slot's h row).
+bool moe1_supported(int top_k, int inter, bool shared);
+hipError_t moe1_launch(const Moe1Args& a, hipStream_t s);
 
 }  // namespace bfp

@@ -9,6 +9,7 @@
 // order) + g_t * shared_t, a fixed order, so the result does not depend on scheduling.
 #include "bfp_moe.hpp"
 #include "gemv_impl.hpp"
+#include "moe_topk.hpp"
 
 namespace bfp {
 
@@ -164,7 +165,154 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   *reinterpret_cast<f32x4*>(a.y + (int64_t)t * a.hidden + n4 * 4) = acc;
 }
 
+// ---- one token ----------------------------------------------------------------------------
+
+// Gate/up + SwiGLU of slot d = blockIdx.y (d == top_k: the shared expert), rows
+// [blockIdx.x * RPW, +RPW) of it: the tile of the grouped kernel with one activation row.
+template <int LPR>
+__global__ __launch_bounds__(kMoeThreads) void moe1_gateup_kernel(Moe1Args ma, int kc) {
+  extern __shared__ uint32_t xs[];
+  __shared__ int xrow[1], yrow[1], sel[1];
+  const int d = blockIdx.y;
+  const bool shared = d == ma.top_k;
+  if (threadIdx.x < kWave && !shared) {
+    const int lane = threadIdx.x;
+    double sel_l[8];
+    int sel_e[8];
+    tk::topk_select(ma.logits, ma.n_exp, ma.top_k, lane, sel_l, sel_e);
+    int e = sel_e[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+      if (j == d) e = sel_e[j];
+    if (blockIdx.x == 0 && d == 0)
+      tk::topk_store(ma.logits, ma.n_exp, ma.top_k, ma.gate_row != 0, lane, sel_l, sel_e, ma.ids, ma.w,
+                     ma.sg_code ? ma.g : nullptr, nullptr);
+    if (lane == 0) sel[0] = e;
+  }
+  if (threadIdx.x == 0) {
+    xrow[0] = 0;
+    yrow[0] = d;
+    if (shared) sel[0] = 0;
+  }
+  __syncthreads();
+  const int64_t nbk = ma.hidden / kBlock;
+  const int64_t rows0 = shared ? 0 : (int64_t)sel[0] * ma.inter;
+  GemvArgs a;
+  a.exp0 = (shared ? ma.sg_exp : ma.g_exp) + rows0 * nbk;
+  a.code0 = (shared ? ma.sg_code : ma.g_code) + rows0 * (ma.hidden / 2);
+  a.exp1 = (shared ? ma.su_exp : ma.u_exp) + rows0 * nbk;
+  a.code1 = (shared ? ma.su_code : ma.u_code) + rows0 * (ma.hidden / 2);
+  a.x = ma.x; a.ldx = ma.hidden;
+  a.y = ma.h; a.ldy = ma.inter; a.y_bf16 = 0;
+  a.n = ma.inter; a.k = ma.hidden; a.m = 1; a.kc = kc;
+  constexpr int RPW = (kMoeThreads / kWave) * (kWave / LPR);
+  run_tile<2, true, 1, LPR>(a, blockIdx.x * RPW, xrow, yrow, xs);
+}
+
+// Down projection + combine for output columns [blockIdx.x * RPW, +RPW): wave d computes
+// slot d's values (the grouped kernel's lane split, groups and reduction for one activation
+// row), then y = sum_j w_j o_j in rank order + g o_shared, as the combine kernel does.
+template <int LPR>
+__global__ __launch_bounds__(kWave * 9) void moe1_down_kernel(Moe1Args ma) {
+  extern __shared__ uint32_t xs[];                 // every slot's h row, fp32 LDS layout
+  constexpr int RPW = kWave / LPR;
+  constexpr int BPU = 2;
+  using L = XLayout<false, 32>;
+  using GroupT = Group<4, BPU, 2, 1, 1>;
+  __shared__ float os[9][RPW];
+  const int ns = blockDim.x / kWave;               // slots: top_k (+ 1 shared)
+  const int d = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const bool shared = d == ma.top_k;
+  const int e = shared ? 0 : ma.ids[d];
+  const int nbk = ma.inter / kBlock;
+  const int nuc = ma.inter / 32;
+  const int64_t rows0 = shared ? 0 : (int64_t)e * ma.hidden;
+  const uint8_t* expm[1] = {(shared ? ma.sd_exp : ma.d_exp) + rows0 * nbk};
+  const uint8_t* codem[1] = {(shared ? ma.sd_code : ma.d_code) + rows0 * (ma.inter / 2)};
+  const int grp = lane / LPR, p = lane % LPR;
+  const int col = blockIdx.x * RPW + grp;
+  bool rowok[1] = {col < ma.hidden};
+  int64_t rowc[1] = {rowok[0] ? col : ma.hidden - 1};
+  constexpr int STEP = 2 * LPR;
+  const int ng = (nuc + STEP - 1) / STEP;          // 1 or 2 (inter <= 64 LPR values)
+  GroupT ga, gb;
+  load_group<4, BPU, 2, 1, 1, LPR>(ga, codem, expm, rowc, ma.inter, nbk, 0, 0, p, nuc);
+  if (ng > 1) load_group<4, BPU, 2, 1, 1, LPR>(gb, codem, expm, rowc, ma.inter, nbk, 0, STEP, p, nuc);
+  const int per_row = ma.inter / 4;
+  for (int idx = threadIdx.x; idx < ns * per_row; idx += blockDim.x) {
+    const int mi = idx / per_row, c4 = idx % per_row;
+    const uint4 v = *reinterpret_cast<const uint4*>(ma.h + (int64_t)mi * ma.inter + c4 * 4);
+    const int kk = c4 * 4;
+    *reinterpret_cast<uint4*>(xs + ((size_t)mi * nuc + kk / 32) * L::kStrideDw + (kk % 32)) = v;
+  }
+  __syncthreads();
+  float acc[1][1][1] = {{{0.f}}};
+  const uint32_t* xd = xs + (size_t)d * nuc * L::kStrideDw;
+  compute_group<4, 1, BPU, 2, 1, 1, false>(acc, ga, rowok, xd, nuc);
+  if (ng > 1) compute_group<4, 1, BPU, 2, 1, 1, false>(acc, gb, rowok, xd, nuc);
+  float v[1] = {acc[0][0][0]};
+  LaneReduce<1, 1, LPR>::run(v, lane);
+  if (p == 0) os[d][grp] = v[0];
+  __syncthreads();
+  const int c = blockIdx.x * RPW + (int)threadIdx.x;
+  if ((int)threadIdx.x < RPW && c < ma.hidden) {
+    float y = 0.f;
+    for (int j = 0; j < ma.top_k; ++j) y = __builtin_fmaf(ma.w[j], os[j][threadIdx.x], y);
+    if (ma.sd_code) y = __builtin_fmaf(ma.g[0], os[ma.top_k][threadIdx.x], y);
+    ma.y[c] = y;
+  }
+}
+
+// Lanes per row as the grouped kernels pick them from K (launch_mbmax).
+inline int moe_lpr(int k) {
+  const int units = k / 32;
+  return units <= 16 ? 4 : units <= 32 ? 8 : 16;
+}
+
+template <int LPR>
+hipError_t moe1_gateup(const Moe1Args& a, hipStream_t s) {
+  using L = XLayout<true, 32>;
+  const int kc = pick_kc(a.hidden, 1, 32, LPR, L::kBytesPerValue);
+  const size_t lds = (size_t)(kc / 32) * L::kStrideDw * sizeof(uint32_t);
+  constexpr int RPW = (kMoeThreads / kWave) * (kWave / LPR);
+  const dim3 grid((a.inter + RPW - 1) / RPW, a.top_k + (a.sg_code ? 1 : 0));
+  hipLaunchKernelGGL(moe1_gateup_kernel<LPR>, grid, dim3(kMoeThreads), lds, s, a, kc);
+  return hipGetLastError();
+}
+
+template <int LPR>
+hipError_t moe1_down(const Moe1Args& a, hipStream_t s) {
+  using L = XLayout<false, 32>;
+  const int ns = a.top_k + (a.sd_code ? 1 : 0);
+  const size_t lds = (size_t)ns * (a.inter / 32) * L::kStrideDw * sizeof(uint32_t);
+  constexpr int RPW = kWave / LPR;
+  hipLaunchKernelGGL(moe1_down_kernel<LPR>, dim3((a.hidden + RPW - 1) / RPW), dim3(kWave * ns), lds, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool moe1_supported(int top_k, int inter, bool shared) {
+  // the down kernel's LDS: every slot's h row, 144 bytes per 32 values (at most 83 KB)
+  (void)shared;
+  return top_k >= 1 && top_k <= 8 && inter % 32 == 0 && inter <= 2048;
+}
+
+hipError_t moe1_launch(const Moe1Args& a, hipStream_t s) {
+  if (!moe1_supported(a.top_k, a.inter, a.sg_code != nullptr)) return hipErrorInvalidValue;
+  hipError_t e;
+  switch (moe_lpr(a.hidden)) {
+    case 4: e = moe1_gateup<4>(a, s); break;
+    case 8: e = moe1_gateup<8>(a, s); break;
+    default: e = moe1_gateup<16>(a, s); break;
+  }
+  if (e != hipSuccess) return e;
+  switch (moe_lpr(a.inter)) {
+    case 4: return moe1_down<4>(a, s);
+    case 8: return moe1_down<8>(a, s);
+    default: return moe1_down<16>(a, s);
+  }
+}
 
 hipError_t moe_gemv_launch(const MoeGemvArgs& a, int nmat, hipStream_t s) {
   if (nmat == 2) return a.x_bf16 ? launch_x<2, true>(a, s) : launch_x<2, false>(a, s);

@@ -15,6 +15,7 @@
 //    bitmaps and popcounts, so every integer result is deterministic.
 #include "bfp_device.hpp"
 #include "bfp_moe.hpp"
+#include "moe_topk.hpp"
 
 // Many-token routing (prefill) is certified rather than computed in fp64 for every expert:
 //  1. approximate logits L~ = x . w_e on the bf16 matrix cores, fp32 accumulation over up
@@ -35,39 +36,9 @@ namespace bfp {
 
 namespace {
 
-// Cross-lane moves without LDS: DPP inside each 16-lane row (partners l^1, l^2, the mirror
-// inside the 8-lane half, l^8), then the four row results read back with v_readlane. Every
-// lane ends with the same value, combined in a fixed order.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i32(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true); }
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const long long b = __double_as_longlong(v);
-  const int lo = dpp_i32<CTRL>((int)(b & 0xffffffffll)), hi = dpp_i32<CTRL>((int)(b >> 32));
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-__device__ __forceinline__ double readlane_f64(double v, int l) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-// wave-wide maximum (fp64 max is exact, so the combination order does not matter)
-__device__ __forceinline__ double wave_max_f64(double v) {
-  v = fmax(v, dpp_f64<kDppQuadXor1>(v));
-  v = fmax(v, dpp_f64<kDppQuadXor2>(v));
-  v = fmax(v, dpp_f64<kDppHalfMirror>(v));
-  v = fmax(v, dpp_f64<kDppRowRor8>(v));
-  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  v += dpp_f64<kDppQuadXor1>(v);
-  v += dpp_f64<kDppQuadXor2>(v);
-  v += dpp_f64<kDppHalfMirror>(v);
-  v += dpp_f64<kDppRowRor8>(v);
-  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
-}
+using tk::readlane_f64;
+using tk::wave_max_f64;
+using tk::wave_sum_f64;
 
 // One wave per (token, 4 experts). Expert index n_exp is the shared-expert gate row.
 __global__ __launch_bounds__(256) void router_logits_kernel(RouteArgs a) {
@@ -128,58 +99,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouteArgs a) {
 // eid, the selected experts also go to eid[t * top_k + j] (LDS bytes).
 __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, uint8_t* eid) {
   const double* l = a.logits + (int64_t)t * a.ld_logits;
-  constexpr int kPer = 4;                                   // n_exp <= 256
-  double v[kPer];
-  int ix[kPer];
-  bool live[kPer];                                          // not selected yet
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    ix[q] = lane + 64 * q;
-    live[q] = ix[q] < a.n_exp;
-    const double lv = live[q] ? l[ix[q]] : -__builtin_huge_val();
-    v[q] = lv != lv ? -__builtin_huge_val() : lv;         // a NaN logit ranks below every number
-  }
   double sel_l[8];
   int sel_e[8];
-  for (int j = 0; j < a.top_k; ++j) {
-    // the largest remaining logit M (a max-reduction: exact, order-free), then the smallest
-    // unselected expert index holding it: expert 64 q + lane, so the first q with a match, then
-    // its lowest lane (equality ballots, no divergent branch). M is never NaN and at least
-    // n_exp - j >= 1 experts are live, so a match always exists: the ids are distinct and in
-    // range whatever the logits hold.
-    const double M = wave_max_f64(fmax(fmax(v[0], v[1]), fmax(v[2], v[3])));
-    int bi = -1;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const uint64_t b = __ballot(live[q] && v[q] == M);
-      if (bi < 0 && b != 0) bi = 64 * q + __builtin_ctzll(b);
-    }
-    sel_l[j] = M;
-    sel_e[j] = bi;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if (ix[q] == bi) { v[q] = -__builtin_huge_val(); live[q] = false; }
-  }
-  // lane j < top_k: exp(l_j - l_0) in fp64; the sum is taken in rank order (a fixed order)
-  double ex = 0.0;
-  double lj = sel_l[0];
-  int ej = sel_e[0];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j == lane && j < a.top_k) { lj = sel_l[j]; ej = sel_e[j]; }
-  if (lane < a.top_k) ex = exp(lj - sel_l[0]);
-  double z = 0.0;
-  for (int j = 0; j < a.top_k; ++j) z += __shfl(ex, j);
-  if (lane < a.top_k) {
-    a.ids[(int64_t)t * a.top_k + lane] = ej;
-    a.w[(int64_t)t * a.top_k + lane] = (float)(ex / z);
-    if (eid) eid[t * a.top_k + lane] = (uint8_t)ej;
-  }
-  if (a.g && lane == 63) {
-    float gv = 1.0f;
-    if (a.sh_gate_w) gv = (float)(1.0 / (1.0 + exp(-l[a.n_exp])));
-    a.g[t] = gv;
-  }
+  tk::topk_select(l, a.n_exp, a.top_k, lane, sel_l, sel_e);
+  tk::topk_store(l, a.n_exp, a.top_k, a.sh_gate_w != nullptr, lane, sel_l, sel_e, a.ids + (int64_t)t * a.top_k,
+                 a.w + (int64_t)t * a.top_k, a.g ? a.g + t : nullptr, eid ? eid + t * a.top_k : nullptr);
 }
 
 // One wave per token.
@@ -808,6 +732,13 @@ hipError_t dispatch_launch(const DispatchArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t router_logits_launch(const RouteArgs& a, hipStream_t s) {
+  if (a.m > 32) return hipErrorInvalidValue;
+  const int rows = a.n_exp + (a.sh_gate_w ? 1 : 0);
+  hipLaunchKernelGGL(router_logits_kernel, dim3((rows + 15) / 16, a.m), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

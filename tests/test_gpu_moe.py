@@ -91,9 +91,11 @@ def test_moe_decode_matches_oracle(moe_full, m):
     note(f"moe decode m={m}")
     x = synth.moe_tokens(m, 0)
     ids = torch.empty((m, 8), dtype=torch.int32, device="cuda")
-    y = bfq.bfp_moe_forward(dev, dev_bf16(x), topk_ids=ids).cpu().numpy()
+    w = torch.empty((m, 8), dtype=torch.float32, device="cuda")
+    y = bfq.bfp_moe_forward(dev, dev_bf16(x), topk_ids=ids, topk_w=w).cpu().numpy()
     rt = oracle.route(x, layer["router"], 8, sh_gate_bits=layer["sh_gate_w"])
     assert np.array_equal(ids.cpu().numpy(), rt["ids"])
+    assert np.allclose(w.cpu().numpy(), rt["r"], rtol=1e-6, atol=0)
     ref, norm = oracle.moe_decode(bank, x, rt)
     assert_within(y, ref, norm, TOL, what=f"moe decode m={m}")
 
@@ -244,6 +246,40 @@ def test_moe_decode_extreme_exponents(m):
     ref, norm = oracle.moe_decode(LazyBank(layer), x, rt)
     assert np.all(np.isfinite(y))
     assert_within(y, ref, norm, TOL, what="moe decode extreme exponents")
+
+
+# (experts, top_k, hidden, inter, shared): lanes per row 4 / 8 / 16 in the gate/up and down
+# kernels, a half-filled last row tile (inter 96), a one-unit second group (inter 1056), no
+# shared expert, top-1, and an intermediate size past the one-token kernels' limit (2080)
+_ONE_TOKEN_SHAPES = [(16, 4, 256, 96, True), (32, 8, 1024, 640, False), (4, 2, 2080, 1056, True),
+                     (8, 1, 128, 2080, True), (6, 3, 512, 512, False)]
+
+
+@pytest.mark.parametrize("n_exp,top_k,hidden,inter,shared", _ONE_TOKEN_SHAPES)
+def test_moe_one_token_shapes(n_exp, top_k, hidden, inter, shared):
+    """One token against the oracle (ids, weights, gate, y), and the same bits as that token's
+    row of a 3-token call (the grouped expert kernels)."""
+    note(f"moe one token E={n_exp} k={top_k} H={hidden} F={inter} shared={shared}")
+    layer = _small_layer(50 + top_k, n_exp=n_exp, hidden=hidden, inter=inter, top_k=top_k)
+    if not shared:
+        for name in ("sh_gate", "sh_up", "sh_down"):
+            layer[name] = np.zeros_like(layer[name])
+    dev = device_layer(layer, shared=shared)
+    rng = np.random.default_rng(51)
+    x = synth.bf16_bits(rng.standard_normal((3, hidden)).astype(np.float32))
+    xd = dev_bf16(x)
+    ids = torch.empty((1, top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, top_k), dtype=torch.float32, device="cuda")
+    y1 = bfq.bfp_moe_forward(dev, xd[1:2].contiguous(), topk_ids=ids, topk_w=w)
+    rt = oracle.route(x[1:2], layer["router"], top_k, sh_gate_bits=layer["sh_gate_w"] if shared else None)
+    assert np.array_equal(ids.cpu().numpy(), rt["ids"])
+    assert np.allclose(w.cpu().numpy(), rt["r"], rtol=1e-6, atol=0)
+    if not shared:
+        rt["g"] = np.zeros(1)              # no shared term (its weights are zero as well)
+    ref, norm = oracle.moe_decode(LazyBank(layer), x[1:2], rt)
+    assert_within(y1.cpu().numpy(), ref, norm, TOL, what="moe one token")
+    y3 = bfq.bfp_moe_forward(dev, xd)
+    assert torch.equal(y1.view(torch.int32), y3[1:2].view(torch.int32))
 
 
 @pytest.mark.parametrize("m", [4, 40])
