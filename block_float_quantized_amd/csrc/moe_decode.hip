@@ -223,6 +223,13 @@ __global__ __launch_bounds__(kWave * 9) void moe1_down_kernel(Moe1Args ma) {
   const int ns = blockDim.x / kWave;               // slots: top_k (+ 1 shared)
   const int d = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const bool shared = d == ma.top_k;
+  // the combine's factors, read now so that their latency overlaps the weights'
+  float wf[9];
+  if ((int)threadIdx.x < RPW) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wf[j] = j < ma.top_k ? ma.w[j] : 0.f;
+    wf[8] = ma.sd_code ? ma.g[0] : 0.f;
+  }
   const int e = shared ? 0 : ma.ids[d];
   const int nbk = ma.inter / kBlock;
   const int nuc = ma.inter / 32;
@@ -257,8 +264,10 @@ __global__ __launch_bounds__(kWave * 9) void moe1_down_kernel(Moe1Args ma) {
   const int c = blockIdx.x * RPW + (int)threadIdx.x;
   if ((int)threadIdx.x < RPW && c < ma.hidden) {
     float y = 0.f;
-    for (int j = 0; j < ma.top_k; ++j) y = __builtin_fmaf(ma.w[j], os[j][threadIdx.x], y);
-    if (ma.sd_code) y = __builtin_fmaf(ma.g[0], os[ma.top_k][threadIdx.x], y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < ma.top_k) y = __builtin_fmaf(wf[j], os[j][threadIdx.x], y);
+    if (ma.sd_code) y = __builtin_fmaf(wf[8], os[ma.top_k][threadIdx.x], y);
     ma.y[c] = y;
   }
 }

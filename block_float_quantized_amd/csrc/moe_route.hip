@@ -40,20 +40,24 @@ using tk::readlane_f64;
 using tk::wave_max_f64;
 using tk::wave_sum_f64;
 
-// One wave per (token, 4 experts). Expert index n_exp is the shared-expert gate row.
+// One wave per (token, R experts). Expert index n_exp is the shared-expert gate row. Each
+// logit is the same sum (chunk order, then the wave reduction) whatever R is.
+template <int R>
 __global__ __launch_bounds__(256) void router_logits_kernel(RouteArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.y;
-  const int e0 = (blockIdx.x * 4 + wave) * 4;
+  const int e0 = (blockIdx.x * 4 + wave) * R;
   const int rows = a.n_exp + (a.sh_gate_w ? 1 : 0);
   if (e0 >= rows) return;
   const uint16_t* xr = a.x + (int64_t)t * a.hidden;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  const int chunks = a.hidden / 8;
-  const uint16_t* wr[4];
+  double acc[R];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < R; ++q) acc[q] = 0.0;
+  const int chunks = a.hidden / 8;
+  const uint16_t* wr[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
     const int e = min(e0 + q, rows - 1);       // rows past the end re-read the last one, unused
     wr[q] = (e < a.n_exp) ? a.router_w + (int64_t)e * a.hidden : a.sh_gate_w;
   }
@@ -61,20 +65,20 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouteArgs a) {
   // branch) before any product; the sums keep the chunk order
   constexpr int kU = 4;
   for (int c0 = lane; c0 < chunks; c0 += 64 * kU) {
-    uint4 xv[kU], wv[kU][4];
+    uint4 xv[kU], wv[kU][R];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int c = min(c0 + 64 * u, chunks - 1);
       xv[u] = *reinterpret_cast<const uint4*>(xr + c * 8);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wv[u][q] = *reinterpret_cast<const uint4*>(wr[q] + c * 8);
+      for (int q = 0; q < R; ++q) wv[u][q] = *reinterpret_cast<const uint4*>(wr[q] + c * 8);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (c0 + 64 * u >= chunks) break;
       const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < R; ++q) {
         const uint32_t ww[4] = {wv[u][q].x, wv[u][q].y, wv[u][q].z, wv[u][q].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouteArgs a) {
     }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < R; ++q) {
     const int e = e0 + q;
     const double s = wave_sum_f64(acc[q]);
     if (lane == 0 && e < rows) {
@@ -686,6 +690,9 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
 
 }  // namespace
 
+// Router rows per wave for m <= 32 (more waves in flight for these short calls).
+constexpr int kDecodeRouterRows = 1;
+
 size_t route_workspace_bytes(int m, int n_exp) {
   const size_t fp64 = (size_t)m * (n_exp + 1) * sizeof(double);
   const int ld = (n_exp + 1 + kRE - 1) / kRE * kRE;
@@ -712,8 +719,8 @@ hipError_t router_launch(const RouteArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const int rows = a.n_exp + (a.sh_gate_w ? 1 : 0);
-  dim3 grid((rows + 15) / 16, a.m);
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, a);
+  dim3 grid((rows + 4 * kDecodeRouterRows - 1) / (4 * kDecodeRouterRows), a.m);
+  hipLaunchKernelGGL(router_logits_kernel<kDecodeRouterRows>, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_kernel, dim3((a.m + 3) / 4), dim3(256), 0, s, a);
@@ -738,14 +745,16 @@ hipError_t dispatch_launch(const DispatchArgs& a, hipStream_t s) {
 hipError_t router_logits_launch(const RouteArgs& a, hipStream_t s) {
   if (a.m > 32) return hipErrorInvalidValue;
   const int rows = a.n_exp + (a.sh_gate_w ? 1 : 0);
-  hipLaunchKernelGGL(router_logits_kernel, dim3((rows + 15) / 16, a.m), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(router_logits_kernel<kDecodeRouterRows>, dim3((rows + 4 * kDecodeRouterRows - 1) / (4 * kDecodeRouterRows), a.m),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t route_dispatch_launch(const RouteArgs& r, const DispatchArgs& d, hipStream_t s) {
   if (r.m > 32 || r.m * r.top_k > kDecodeMaxPairs) return hipErrorInvalidValue;
   const int rows = r.n_exp + (r.sh_gate_w ? 1 : 0);
-  hipLaunchKernelGGL(router_logits_kernel, dim3((rows + 15) / 16, r.m), dim3(256), 0, s, r);
+  hipLaunchKernelGGL(router_logits_kernel<kDecodeRouterRows>, dim3((rows + 4 * kDecodeRouterRows - 1) / (4 * kDecodeRouterRows), r.m),
+                     dim3(256), 0, s, r);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_dispatch_kernel, dim3(1), dim3(kDispThreads), 0, s, r, d);

@@ -44,40 +44,87 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
+// Wave-wide maximum of an unsigned 32-bit value, in every lane: DPP inside each 16-lane row,
+// then v_permlane16_swap and v_permlane32_swap across rows (no scalar round trip).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i32<kDppQuadXor1>((int)v));
+  v = max(v, (uint32_t)dpp_i32<kDppQuadXor2>((int)v));
+  v = max(v, (uint32_t)dpp_i32<kDppHalfMirror>((int)v));
+  v = max(v, (uint32_t)dpp_i32<kDppRowRor8>((int)v));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)r16[0], (uint32_t)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)r32[0], (uint32_t)r32[1]);
+}
+
+// A 64-bit key whose unsigned order is the numeric order of fp64 logits: NaN is taken as -inf
+// (it ranks below every number) and -0 as +0 (equal values tie). Every logit's key is at least
+// key(-inf) > 0, so 0 marks an empty slot.
+__device__ __forceinline__ uint64_t order_key(double v) {
+  if (v != v) v = -__builtin_huge_val();
+  if (v == 0.0) v = 0.0;
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | (1ull << 63));
+}
+__device__ __forceinline__ double key_value(uint64_t k) {
+  return __longlong_as_double((long long)((k >> 63) ? (k & ~(1ull << 63)) : ~k));
+}
+
 // The top_k experts of one token (logits l[0..n_exp), fp64) by (logit descending, expert
 // ascending), computed by one wave: sel_e / sel_l in rank order, the same in every lane.
 // n_exp <= 256, top_k <= 8.
+//
+// Lane p holds experts 4p .. 4p+3 as keys, sorted (key descending, expert ascending); each
+// round takes the largest head key over the wave (high words, then the low words of the lanes
+// that tie on them) and the lowest lane holding it, which holds the lowest such expert, and
+// that lane drops its head. The keys are distinct per (value, expert) order, so the result is
+// the plain sort's; at least n_exp - j >= 1 live keys remain in round j, so the ids are
+// distinct and in range whatever the logits hold.
 __device__ __forceinline__ void topk_select(const double* l, int n_exp, int top_k, int lane, double (&sel_l)[8],
                                             int (&sel_e)[8]) {
-  constexpr int kPer = 4;                                   // n_exp <= 256
-  double v[kPer];
-  int ix[kPer];
-  bool live[kPer];                                          // not selected yet
+  uint64_t k[4];
+  int ix[4];
+  double lv[4];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    ix[q] = lane + 64 * q;
-    live[q] = ix[q] < n_exp;
-    const double lv = live[q] ? l[ix[q]] : -__builtin_huge_val();
-    v[q] = lv != lv ? -__builtin_huge_val() : lv;         // a NaN logit ranks below every number
+  for (int q = 0; q < 4; ++q) {                      // every load issued before any use
+    ix[q] = 4 * lane + q;
+    lv[q] = l[min(ix[q], n_exp - 1)];
   }
-  for (int j = 0; j < top_k; ++j) {
-    // the largest remaining logit M (a max-reduction: exact, order-free), then the smallest
-    // unselected expert index holding it: expert 64 q + lane, so the first q with a match, then
-    // its lowest lane (equality ballots, no divergent branch). M is never NaN and at least
-    // n_exp - j >= 1 experts are live, so a match always exists: the ids are distinct and in
-    // range whatever the logits hold.
-    const double M = wave_max_f64(fmax(fmax(v[0], v[1]), fmax(v[2], v[3])));
-    int bi = -1;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const uint64_t b = __ballot(live[q] && v[q] == M);
-      if (bi < 0 && b != 0) bi = 64 * q + __builtin_ctzll(b);
+  for (int q = 0; q < 4; ++q) k[q] = order_key(lv[q]) & (ix[q] < n_exp ? ~0ull : 0ull);
+  // sorting network on (key descending, expert ascending)
+  auto cx = [&](int a, int b) {
+    const bool swap = k[b] > k[a] || (k[b] == k[a] && ix[b] < ix[a]);
+    const uint64_t ka = k[a];
+    const int ia = ix[a];
+    k[a] = swap ? k[b] : k[a];
+    ix[a] = swap ? ix[b] : ix[a];
+    k[b] = swap ? ka : k[b];
+    ix[b] = swap ? ia : ix[b];
+  };
+  cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= top_k) break;
+    const uint32_t hh = (uint32_t)(k[0] >> 32), hl = (uint32_t)k[0];
+    const uint32_t mh = wave_max_u32(hh);
+    uint64_t b = __ballot(hh == mh);
+    uint32_t ml;
+    if (__popcll(b) > 1) {
+      ml = wave_max_u32(hh == mh ? hl : 0u);
+      b = __ballot(hh == mh && hl == ml);
+    } else {
+      ml = (uint32_t)__builtin_amdgcn_readlane((int)hl, __builtin_ctzll(b));
     }
-    sel_l[j] = M;
-    sel_e[j] = bi;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if (ix[q] == bi) { v[q] = -__builtin_huge_val(); live[q] = false; }
+    const int wl = __builtin_ctzll(b);
+    sel_l[j] = key_value(((uint64_t)mh << 32) | ml);
+    sel_e[j] = __builtin_amdgcn_readlane(ix[0], wl);
+    if (lane == wl) {
+      k[0] = k[1]; ix[0] = ix[1];
+      k[1] = k[2]; ix[1] = ix[2];
+      k[2] = k[3]; ix[2] = ix[3];
+      k[3] = 0ull;
+    }
   }
 }
 
