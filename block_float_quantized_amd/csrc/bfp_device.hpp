@@ -240,6 +240,8 @@ __device__ __forceinline__ void butterfly_x16(float* v) {
 template <int C, int KEEP, int LPR>
 struct LaneReduce {
   static constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+  static_assert(C >= 1 && (C & (C - 1)) == 0 && LPR >= 1 && (LPR & (LPR - 1)) == 0,
+                "the halving tree takes a power-of-two count of values and lanes");
   static constexpr int kSteps = ilog2(LPR);
   static constexpr int kHalvings = (ilog2(C / KEEP) < kSteps) ? ilog2(C / KEEP) : kSteps;
   static constexpr int kCount = C >> kHalvings;

@@ -9,9 +9,10 @@
 //
 // Design:
 //  * K is cut into steps of SK = 128 G values (G from the format alone) and the steps into
-//    KS slices (KS from N and K alone). Workgroup (c, s) owns 64 output columns (16 per wave,
-//    of each matrix) over slice s: its four waves walk the same K positions in lockstep, so the
-//    activations staged in LDS for them are one short window shared by all four.
+//    KS slices (KS from N and K alone). Workgroup (c, s) owns 128 output columns (16 per wave,
+//    of each matrix) over slice s: its eight waves walk the same K positions in lockstep, so
+//    the activations staged in LDS for them are one short window shared by all eight (wider
+//    workgroups stage each activation row for more columns).
 //  * In a step, lane l takes weight row l % 16 and the SK / 4 consecutive values starting at
 //    (l / 16) SK / 4: G 16-byte loads (BFP4) or 2G (BFP8) plus one load of its 2G exponent
 //    bytes. Every weight byte is loaded once, straight into registers, one step ahead of use.
@@ -39,7 +40,7 @@ namespace mg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = 4;                   // waves per workgroup (columns: 16 per wave)
+constexpr int kWaves = 8;                   // waves per workgroup (columns: 16 per wave)
 constexpr int kCols = 16 * kWaves;          // output columns per workgroup
 constexpr int kLdsStage = 40 * 1024;        // LDS budget for staged activations
 
