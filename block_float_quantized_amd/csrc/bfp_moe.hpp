@@ -85,28 +85,34 @@ struct CombineArgs {
 };
 hipError_t combine_launch(const CombineArgs& a, hipStream_t s);
 
-// One token in two launches after the router logits: (1) every workgroup of the gate/up grid
-// ranks the experts itself from the logits and streams its rows of the selected expert of its
-// slot (slot top_k: the shared expert); one of them also writes ids, w and g; (2) each
-// workgroup of the down grid computes a few output columns of every slot's down projection
-// and combines them. The per-row arithmetic is that of the grouped kernels above (same tile,
-// same lane split and order), so a token's output does not depend on the batch size.
-struct Moe1Args {
-  const double* logits;                             // [n_exp + 1] (the last: shared-gate logit)
-  int n_exp, top_k;
+// Per-token path, two launches after the router logits: (1) every workgroup of the gate/up
+// grid ranks its token's experts itself from the logits and streams its rows of the expert of
+// its (token, slot) (slot top_k: the shared expert); one per token also writes that token's
+// ids, w and g; (2) each workgroup of the down grid computes a few output columns of every
+// slot of one token and combines them. No dispatch, no per-pair outputs: an expert chosen by
+// several tokens is streamed once per token. The per-row arithmetic is that of the grouped
+// kernels above (same tile, same lane split and order), so a token's output does not depend on
+// the batch size or on which path ran.
+struct MoeTokArgs {
+  const double* logits;                             // [m][ld_logits] (column n_exp: shared gate)
+  int ld_logits;
+  int m, n_exp, top_k;
   int gate_row;                                     // a shared-gate logit is present
-  const uint16_t* x;                                // bf16 [hidden]
+  const uint16_t* x;                                // bf16 [m][hidden]
   int hidden, inter;
   const uint8_t *g_exp, *g_code, *u_exp, *u_code, *d_exp, *d_code;       // routed, stacked
   const uint8_t *sg_exp, *sg_code, *su_exp, *su_code, *sd_exp, *sd_code; // shared (null: none)
-  int32_t* ids;                                     // [top_k], rank order
-  float* w;                                         // [top_k]
-  float* g;                                         // [1] (written when there is a shared expert)
-  float* h;                                         // fp32 [top_k + 1][inter], row = slot
-  float* y;                                         // fp32 [hidden]
+  int32_t* ids;                                     // [m][top_k], rank order
+  float* w;                                         // [m][top_k]
+  float* g;                                         // [m] (written when there is a shared expert)
+  float* h;                                         // fp32 [m][top_k + 1][inter]
+  float* y;                                         // fp32 [m][hidden]
 };
-// Whether the one-token kernels take this layer (the down kernel stages every slot's h row).
-bool moe1_supported(int top_k, int inter, bool shared);
-hipError_t moe1_launch(const Moe1Args& a, hipStream_t s);
+// Largest batch the per-token path takes (beyond it the grouped kernels read each selected
+// expert once for all of its tokens).
+constexpr int kTokPathMaxM = 4;
+// Whether the per-token kernels take this call (the down kernel stages every slot's h row).
+bool moe_tok_supported(int m, int top_k, int inter);
+hipError_t moe_tok_launch(const MoeTokArgs& a, hipStream_t s);
 
 }  // namespace bfp

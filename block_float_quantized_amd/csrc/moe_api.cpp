@@ -1,5 +1,5 @@
 // C ABI of the MoE entry points: layer checks, workspace layout, and the decode pipelines:
-// one token: router logits -> top-k + gate/up + SwiGLU -> down + combine; 2..32 tokens:
+// a few tokens: router logits -> per-token top-k + gate/up + SwiGLU -> down + combine; more:
 // router logits -> top-k + dispatch -> grouped gate/up + SwiGLU -> grouped down -> combine.
 #include <hip/hip_runtime.h>
 
@@ -177,11 +177,12 @@ int32_t moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, float*
   float* g = at<float>(ws, ly.g);
   const bfp::RouteArgs r = route_args(L, x, m, at<double>(ws, ly.logits), ids, w, g);
   hipError_t e = hipSuccess;
-  if (m == 1 && bfp::moe1_supported(L->top_k, (int)L->inter, shared)) {
-    // one token: router logits, then top-k + gate/up, then down + combine
+  if (bfp::moe_tok_supported((int)m, L->top_k, (int)L->inter)) {
+    // few tokens: router logits, then top-k + gate/up, then down + combine, per token
     if (bfp::router_logits_launch(r, s) != hipSuccess) return BFP_E_DEVICE;
-    bfp::Moe1Args a{};
-    a.logits = r.logits; a.n_exp = L->n_experts; a.top_k = L->top_k; a.gate_row = L->sh_gate_w != nullptr;
+    bfp::MoeTokArgs a{};
+    a.logits = r.logits; a.ld_logits = r.ld_logits;
+    a.m = (int)m; a.n_exp = L->n_experts; a.top_k = L->top_k; a.gate_row = L->sh_gate_w != nullptr;
     a.x = x; a.hidden = (int)L->hidden; a.inter = (int)L->inter;
     a.g_exp = L->gate.exp; a.g_code = L->gate.code; a.u_exp = L->up.exp; a.u_code = L->up.code;
     a.d_exp = L->down.exp; a.d_code = L->down.code;
@@ -191,7 +192,7 @@ int32_t moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, float*
     }
     a.ids = ids; a.w = w; a.g = g;
     a.h = at<float>(ws, ly.h); a.y = y;
-    return from_hip(bfp::moe1_launch(a, s));
+    return from_hip(bfp::moe_tok_launch(a, s));
   }
   bfp::DispatchArgs d{};
   d.ids = ids; d.m = (int)m; d.top_k = L->top_k; d.n_exp = L->n_experts;

@@ -165,33 +165,36 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   *reinterpret_cast<f32x4*>(a.y + (int64_t)t * a.hidden + n4 * 4) = acc;
 }
 
-// ---- one token ----------------------------------------------------------------------------
+// ---- per-token path ------------------------------------------------------------------------
 
-// Gate/up + SwiGLU of slot d = blockIdx.y (d == top_k: the shared expert), rows
-// [blockIdx.x * RPW, +RPW) of it: the tile of the grouped kernel with one activation row.
+// Gate/up + SwiGLU of token t and slot d (blockIdx.y = t * ns + d, ns = top_k + 1 with a
+// shared expert, d == top_k: the shared expert), rows [blockIdx.x * RPW, +RPW) of it: the tile
+// of the grouped kernel with one activation row. h row t * ns + d.
 template <int LPR>
-__global__ __launch_bounds__(kMoeThreads) void moe1_gateup_kernel(Moe1Args ma, int kc) {
+__global__ __launch_bounds__(kMoeThreads) void tok_gateup_kernel(MoeTokArgs ma, int kc) {
   extern __shared__ uint32_t xs[];
   __shared__ int xrow[1], yrow[1], sel[1];
-  const int d = blockIdx.y;
+  const int ns = ma.top_k + (ma.sg_code ? 1 : 0);
+  const int t = blockIdx.y / ns, d = blockIdx.y % ns;
   const bool shared = d == ma.top_k;
+  const double* l = ma.logits + (int64_t)t * ma.ld_logits;
   if (threadIdx.x < kWave && !shared) {
     const int lane = threadIdx.x;
     double sel_l[8];
     int sel_e[8];
-    tk::topk_select(ma.logits, ma.n_exp, ma.top_k, lane, sel_l, sel_e);
+    tk::topk_select(l, ma.n_exp, ma.top_k, lane, sel_l, sel_e);
     int e = sel_e[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j)
       if (j == d) e = sel_e[j];
     if (blockIdx.x == 0 && d == 0)
-      tk::topk_store(ma.logits, ma.n_exp, ma.top_k, ma.gate_row != 0, lane, sel_l, sel_e, ma.ids, ma.w,
-                     ma.sg_code ? ma.g : nullptr, nullptr);
+      tk::topk_store(l, ma.n_exp, ma.top_k, ma.gate_row != 0, lane, sel_l, sel_e, ma.ids + (int64_t)t * ma.top_k,
+                     ma.w + (int64_t)t * ma.top_k, ma.sg_code ? ma.g + t : nullptr, nullptr);
     if (lane == 0) sel[0] = e;
   }
   if (threadIdx.x == 0) {
-    xrow[0] = 0;
-    yrow[0] = d;
+    xrow[0] = t;
+    yrow[0] = blockIdx.y;
     if (shared) sel[0] = 0;
   }
   __syncthreads();
@@ -209,11 +212,12 @@ __global__ __launch_bounds__(kMoeThreads) void moe1_gateup_kernel(Moe1Args ma, i
   run_tile<2, true, 1, LPR>(a, blockIdx.x * RPW, xrow, yrow, xs);
 }
 
-// Down projection + combine for output columns [blockIdx.x * RPW, +RPW): wave d computes
-// slot d's values (the grouped kernel's lane split, groups and reduction for one activation
-// row), then y = sum_j w_j o_j in rank order + g o_shared, as the combine kernel does.
+// Down projection + combine of token t = blockIdx.y for output columns [blockIdx.x * RPW,
+// +RPW): wave d computes slot d's values (the grouped kernel's lane split, groups and
+// reduction for one activation row), then y = sum_j w_j o_j in rank order + g o_shared, as
+// the combine kernel does.
 template <int LPR>
-__global__ __launch_bounds__(kWave * 9) void moe1_down_kernel(Moe1Args ma) {
+__global__ __launch_bounds__(kWave * 9) void tok_down_kernel(MoeTokArgs ma) {
   extern __shared__ uint32_t xs[];                 // every slot's h row, fp32 LDS layout
   constexpr int RPW = kWave / LPR;
   constexpr int BPU = 2;
@@ -221,16 +225,19 @@ __global__ __launch_bounds__(kWave * 9) void moe1_down_kernel(Moe1Args ma) {
   using GroupT = Group<4, BPU, 2, 1, 1>;
   __shared__ float os[9][RPW];
   const int ns = blockDim.x / kWave;               // slots: top_k (+ 1 shared)
+  const int t = blockIdx.y;
   const int d = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const bool shared = d == ma.top_k;
+  const int32_t* ids = ma.ids + (int64_t)t * ma.top_k;
+  const float* wt = ma.w + (int64_t)t * ma.top_k;
   // the combine's factors, read now so that their latency overlaps the weights'
   float wf[9];
   if ((int)threadIdx.x < RPW) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wf[j] = j < ma.top_k ? ma.w[j] : 0.f;
-    wf[8] = ma.sd_code ? ma.g[0] : 0.f;
+    for (int j = 0; j < 8; ++j) wf[j] = j < ma.top_k ? wt[j] : 0.f;
+    wf[8] = ma.sd_code ? ma.g[t] : 0.f;
   }
-  const int e = shared ? 0 : ma.ids[d];
+  const int e = shared ? 0 : ids[d];
   const int nbk = ma.inter / kBlock;
   const int nuc = ma.inter / 32;
   const int64_t rows0 = shared ? 0 : (int64_t)e * ma.hidden;
@@ -246,9 +253,10 @@ __global__ __launch_bounds__(kWave * 9) void moe1_down_kernel(Moe1Args ma) {
   load_group<4, BPU, 2, 1, 1, LPR>(ga, codem, expm, rowc, ma.inter, nbk, 0, 0, p, nuc);
   if (ng > 1) load_group<4, BPU, 2, 1, 1, LPR>(gb, codem, expm, rowc, ma.inter, nbk, 0, STEP, p, nuc);
   const int per_row = ma.inter / 4;
+  const float* ht = ma.h + (int64_t)t * ns * ma.inter;
   for (int idx = threadIdx.x; idx < ns * per_row; idx += blockDim.x) {
     const int mi = idx / per_row, c4 = idx % per_row;
-    const uint4 v = *reinterpret_cast<const uint4*>(ma.h + (int64_t)mi * ma.inter + c4 * 4);
+    const uint4 v = *reinterpret_cast<const uint4*>(ht + (int64_t)mi * ma.inter + c4 * 4);
     const int kk = c4 * 4;
     *reinterpret_cast<uint4*>(xs + ((size_t)mi * nuc + kk / 32) * L::kStrideDw + (kk % 32)) = v;
   }
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(kWave * 9) void moe1_down_kernel(Moe1Args ma) {
     for (int j = 0; j < 8; ++j)
       if (j < ma.top_k) y = __builtin_fmaf(wf[j], os[j][threadIdx.x], y);
     if (ma.sd_code) y = __builtin_fmaf(wf[8], os[ma.top_k][threadIdx.x], y);
-    ma.y[c] = y;
+    ma.y[(int64_t)t * ma.hidden + c] = y;
   }
 }
 
@@ -279,47 +287,46 @@ inline int moe_lpr(int k) {
 }
 
 template <int LPR>
-hipError_t moe1_gateup(const Moe1Args& a, hipStream_t s) {
+hipError_t tok_gateup(const MoeTokArgs& a, hipStream_t s) {
   using L = XLayout<true, 32>;
   const int kc = pick_kc(a.hidden, 1, 32, LPR, L::kBytesPerValue);
   const size_t lds = (size_t)(kc / 32) * L::kStrideDw * sizeof(uint32_t);
   constexpr int RPW = (kMoeThreads / kWave) * (kWave / LPR);
-  const dim3 grid((a.inter + RPW - 1) / RPW, a.top_k + (a.sg_code ? 1 : 0));
-  hipLaunchKernelGGL(moe1_gateup_kernel<LPR>, grid, dim3(kMoeThreads), lds, s, a, kc);
+  const dim3 grid((a.inter + RPW - 1) / RPW, a.m * (a.top_k + (a.sg_code ? 1 : 0)));
+  hipLaunchKernelGGL(tok_gateup_kernel<LPR>, grid, dim3(kMoeThreads), lds, s, a, kc);
   return hipGetLastError();
 }
 
 template <int LPR>
-hipError_t moe1_down(const Moe1Args& a, hipStream_t s) {
+hipError_t tok_down(const MoeTokArgs& a, hipStream_t s) {
   using L = XLayout<false, 32>;
   const int ns = a.top_k + (a.sd_code ? 1 : 0);
   const size_t lds = (size_t)ns * (a.inter / 32) * L::kStrideDw * sizeof(uint32_t);
   constexpr int RPW = kWave / LPR;
-  hipLaunchKernelGGL(moe1_down_kernel<LPR>, dim3((a.hidden + RPW - 1) / RPW), dim3(kWave * ns), lds, s, a);
+  hipLaunchKernelGGL(tok_down_kernel<LPR>, dim3((a.hidden + RPW - 1) / RPW, a.m), dim3(kWave * ns), lds, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool moe1_supported(int top_k, int inter, bool shared) {
+bool moe_tok_supported(int m, int top_k, int inter) {
   // the down kernel's LDS: every slot's h row, 144 bytes per 32 values (at most 83 KB)
-  (void)shared;
-  return top_k >= 1 && top_k <= 8 && inter % 32 == 0 && inter <= 2048;
+  return m >= 1 && m <= kTokPathMaxM && top_k >= 1 && top_k <= 8 && inter % 32 == 0 && inter <= 2048;
 }
 
-hipError_t moe1_launch(const Moe1Args& a, hipStream_t s) {
-  if (!moe1_supported(a.top_k, a.inter, a.sg_code != nullptr)) return hipErrorInvalidValue;
+hipError_t moe_tok_launch(const MoeTokArgs& a, hipStream_t s) {
+  if (!moe_tok_supported(a.m, a.top_k, a.inter)) return hipErrorInvalidValue;
   hipError_t e;
   switch (moe_lpr(a.hidden)) {
-    case 4: e = moe1_gateup<4>(a, s); break;
-    case 8: e = moe1_gateup<8>(a, s); break;
-    default: e = moe1_gateup<16>(a, s); break;
+    case 4: e = tok_gateup<4>(a, s); break;
+    case 8: e = tok_gateup<8>(a, s); break;
+    default: e = tok_gateup<16>(a, s); break;
   }
   if (e != hipSuccess) return e;
   switch (moe_lpr(a.inter)) {
-    case 4: return moe1_down<4>(a, s);
-    case 8: return moe1_down<8>(a, s);
-    default: return moe1_down<16>(a, s);
+    case 4: return tok_down<4>(a, s);
+    case 8: return tok_down<8>(a, s);
+    default: return tok_down<16>(a, s);
   }
 }
 
