@@ -64,6 +64,14 @@ def parse():
                     help="only time the MoE workloads (decode and the 2,048-token prefill) and print their lines")
     ap.add_argument("--kernel-summary", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace output folder into a per-kernel markdown table")
+    ap.add_argument("--floor-driver", action="store_true",
+                    help="only time the launch floor: a one-element fill kernel, eager and graph-replayed")
+    ap.add_argument("--busy-segments", action="store_true",
+                    help="after timing each workload, run 20 more calls between two marker kernels "
+                         "(for a per-workload device-busy table from a kernel trace)")
+    ap.add_argument("--segments", metavar="BENCH_STDERR",
+                    help="with --kernel-summary: the stderr of a --busy-segments run; print the "
+                         "device-busy time per call of each workload")
     return ap.parse_args()
 
 
@@ -74,6 +82,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_bfp4_gateup_m1_hbm_traffic.m
 HEADLINE_SOURCES = tuple(f"block_float_quantized_amd/csrc/{f}" for f in (
     "gemv_b4_bf16x.hip", "gemv_row.hpp", "gemv_impl.hpp", "bfp_device.hpp", "bfp_internal.hpp", "argmax.hpp"))
 HEADLINE_KERNEL = "row_gemv_kernel<4, 2, true, 5, false>"
+DOWN_KERNEL = "row_gemv_kernel<4, 1, false, 1, false>"     # the step's down projection
 COPY_BYTES = 512 << 20
 
 
@@ -101,16 +110,19 @@ def recorded_traffic():
 
 
 def pmc_driver():
-    """Launch the headline gate/up kernel over cold replicas and a plain copy of known size."""
+    """Launch the headline gate/up kernel and the step's down projection over cold replicas, and
+    a plain copy of known size."""
     import torch
     import block_float_quantized_amd as bfq
     torch.cuda.set_device(0)
     c, mats = make_mlp(8)
     x = bf16_dev(c["x"])
     h = torch.empty((1, INTER), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, HIDDEN), dtype=torch.bfloat16, device="cuda")
     for i in range(24):
-        g, u, _ = mats[i % len(mats)]
+        g, u, d = mats[i % len(mats)]
         bfq.bfp_gemm(g, x, w_up=u, out=h)
+        bfq.bfp_gemm(d, h, out_dtype=torch.bfloat16, out=y)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(4):
@@ -133,7 +145,8 @@ def pmc_report(fetch_dir: str, write_dir: str):
         for name, cn, v in rows:
             if cn != counter:
                 continue
-            key = "headline" if HEADLINE_KERNEL in name else "copy" if "MulFunctor" in name else None
+            key = ("headline" if HEADLINE_KERNEL in name else "down" if DOWN_KERNEL in name
+                   else "copy" if "MulFunctor" in name else None)
             if key:
                 acc.setdefault(key, []).append(v)
         return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
@@ -152,6 +165,11 @@ def pmc_report(fetch_dir: str, write_dir: str):
     print(f"WRITE_SIZE KiB/dispatch: headline {w['headline']:.1f}, copy {w['copy']:.1f} "
           f"(copy writes {kib:.0f} KiB: factor {fw:.4f})")
     print(f"scaled HBM bytes per launch: read {fetch_b:.0f}, written {write_b:.0f}; algorithmic {alg}")
+    if "down" in f and "down" in w:
+        alg_d = bfq.exp_bytes(HIDDEN, INTER) + bfq.code_bytes(4, HIDDEN, INTER) + INTER * 4 + HIDDEN * 2
+        print(f"down kernel: {DOWN_KERNEL} ({fn['down']} dispatches): FETCH_SIZE {f['down']:.1f} KiB, "
+              f"WRITE_SIZE {w['down']:.1f} KiB per dispatch; scaled read {f['down'] * 1024 * ff:.0f}, "
+              f"written {w['down'] * 1024 * fw:.0f}; algorithmic {alg_d}")
     print(f"traffic_bytes_per_launch: {int(round(fetch_b + write_b))}")
     print(f"kernel_sources_sha256: {headline_sources_sha256()}")
 
@@ -195,6 +213,56 @@ def kernel_summary(trace_dir: str):
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+BUSY = {"on": False}
+BUSY_CALLS = 20
+MARKER_KERNEL = "spin_kernel"      # torch.cuda._sleep
+
+
+def busy_segment(name: str, fn):
+    """BUSY_CALLS calls of fn between two marker kernels (only with --busy-segments): the kernel
+    trace then shows exactly this workload's kernels between the markers."""
+    if not BUSY["on"]:
+        return
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda._sleep(1000)
+    for i in range(BUSY_CALLS):
+        fn(i)
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+    log(f"busy segment: {name}")
+
+
+def segment_summary(trace_dir: str, stderr_file: str):
+    """Device-busy time per call of each workload: the kernels between each pair of marker
+    kernels (in launch order), summed and divided by the calls; also the span from the first
+    kernel's start to the last one's end per call (busy time plus the gaps between kernels)."""
+    import glob
+    import sqlite3
+    names = [l.split("busy segment: ", 1)[1].strip() for l in open(stderr_file) if "busy segment: " in l]
+    db = glob.glob(os.path.join(trace_dir, "**", "*.db"), recursive=True)[0]
+    rows = sorted(sqlite3.connect(db).execute("select name, start, end from kernels").fetchall(),
+                  key=lambda r: r[1])
+    marks = [i for i, r in enumerate(rows) if MARKER_KERNEL in r[0]]
+    print(f"| workload | calls | device busy per call (us) | span per call (us) | kernels per call | largest kernel (share) |")
+    print("|---|---:|---:|---:|---:|---|")
+    for j, name in enumerate(names):
+        if 2 * j + 1 >= len(marks):
+            break
+        seg = rows[marks[2 * j] + 1:marks[2 * j + 1]]
+        if not seg:
+            continue
+        busy = sum(e - b for _, b, e in seg) / 1000.0
+        span = (max(e for _, _, e in seg) - min(b for _, b, _ in seg)) / 1000.0
+        per = {}
+        for n, b, e in seg:
+            k = short_kernel_name(n)
+            per[k] = per.get(k, 0.0) + (e - b) / 1000.0
+        top = max(per.items(), key=lambda kv: kv[1])
+        print(f"| {name} | {BUSY_CALLS} | {busy / BUSY_CALLS:.2f} | {span / BUSY_CALLS:.2f} | "
+              f"{len(seg) / BUSY_CALLS:.1f} | `{top[0]}` ({100 * top[1] / busy:.0f}%) |")
 
 
 def bf16_dev(bits):
@@ -396,6 +464,7 @@ def run_mlp(args, m, mats, xb, batch_invariant=False, graph=False):
 
     ms_step = timed(step, args.steps, args.warmup)
     ms_gu = timed(gateup, args.steps, args.warmup)
+    busy_segment(f"dense BFP4 MLP M={m}" + (" batch-invariant" if batch_invariant else ""), step)
     b = mlp_bytes(m)
     out = {"us_per_call": ms_step * 1e3, "GB/s": b["step"] / (ms_step * 1e-3) / 1e9,
            "gateup_us": ms_gu * 1e3, "gateup_GB/s": b["gateup_kernel"] / (ms_gu * 1e-3) / 1e9,
@@ -548,6 +617,21 @@ def cpu_baseline(c: dict, xbits: np.ndarray) -> dict:
 
 # ---- other workloads -----------------------------------------------------------------------
 
+def launch_floor(args):
+    """The cost of one dependent kernel launch with no work: a fill of one float, eager and as
+    graph-replayed calls (the floor under any short call, one per launch)."""
+    import torch
+    torch.cuda.set_device(0)
+    t = torch.zeros(1, device="cuda")
+    fn = lambda i: t.fill_(float(i % 7))
+    ms = timed(fn, max(args.steps, 1000), args.warmup)
+    g = timed_graph(fn, [t], calls=300, reps=10)
+    out = {"launch floor (one-element fill)": {"us_per_call": round(ms * 1e3, 3),
+                                               "us_per_call_graph": None if g is None else round(g * 1e3, 3)}}
+    log(f"launch floor: {ms * 1e3:.3f} us eager, {out['launch floor (one-element fill)']['us_per_call_graph']} us graph")
+    return out
+
+
 def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32", argmax_name=None):
     """Time bfp_gemm on one matrix over cold replicas for each x in xs_bits (dict M -> bits);
     with argmax_name, also bfp_gemm_argmax (greedy pick per row, no outputs written)."""
@@ -568,6 +652,7 @@ def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32", argmax_name=None
                                 "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                                 "bytes": nbytes, "replicas": R, "tok_per_s": round(m / (ms * 1e-3), 1)}
         add_graph_timing(out[f"{name} M={m}"], fn, [y], nbytes)
+        busy_segment(f"{name} M={m}", fn)
         log(f"{name} M={m}: {ms * 1e3:.2f} us (graph replay {out[f'{name} M={m}']['us_per_call_graph']} us)")
         if argmax_name:
             idx = torch.empty((m,), dtype=torch.int32, device="cuda")
@@ -581,6 +666,7 @@ def gemv_workload(args, name, w, fmt, xs_bits, out_dtype="f32", argmax_name=None
                                            "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                                            "bytes": nbytes, "replicas": R, "tok_per_s": round(m / (ms * 1e-3), 1)}
             add_graph_timing(out[f"{argmax_name} M={m}"], fa, [idx, val], nbytes)
+            busy_segment(f"{argmax_name} M={m}", fa)
             log(f"{argmax_name} M={m}: {ms * 1e3:.2f} us "
                 f"(graph replay {out[f'{argmax_name} M={m}']['us_per_call_graph']} us)")
     del mats
@@ -624,6 +710,7 @@ def attn_workloads(args):
                     "cache_bytes": per, "replicas": R,
                     "bytes_per_token_layer": kvh * row}
         add_graph_timing(out[key], fn, [y], per)
+        busy_segment(key, fn)
         log(f"attention {name} L={L}: {ms * 1e3:.2f} us (graph replay {out[key]['us_per_call_graph']} us)")
         del caches
         torch.cuda.empty_cache()
@@ -667,6 +754,7 @@ def moe_workloads(args):
                                     "distinct_experts": d, "bytes": int(nbytes),
                                     "tok_per_s": round(m / (ms * 1e-3), 1)}
         add_graph_timing(out[f"moe decode M={m}"], fn, [y], int(nbytes))
+        busy_segment(f"moe decode M={m}", fn)
         log(f"moe decode M={m}: {ms * 1e3:.2f} us, {d:.1f} experts "
             f"(graph replay {out[f'moe decode M={m}']['us_per_call_graph']} us)")
     # prefill chunk: 2,048 tokens with the skewed router bias
@@ -682,6 +770,7 @@ def moe_workloads(args):
     used = len(np.unique(ids.cpu().numpy()))
     steps = max(10, args.steps // 10)
     ms = timed(lambda i: bfq.bfp_moe_forward(layers[i % nl], xs[i % 2], out=y, workspace=ws), steps, 3)
+    busy_segment("moe prefill M=2048", lambda i: bfq.bfp_moe_forward(layers[i % nl], xs[i % 2], out=y, workspace=ws))
     flops = 2.0 * (m * 8 + m) * 3 * 2048 * 512
     router_flops = 2.0 * m * 257 * 2048
     tfs = flops / (ms * 1e-3) / 1e12
@@ -697,6 +786,9 @@ def moe_workloads(args):
 
 def main():
     args = parse()
+    if args.kernel_summary and args.segments:
+        segment_summary(args.kernel_summary, args.segments)
+        return
     if args.kernel_summary:
         kernel_summary(args.kernel_summary)
         return
@@ -706,6 +798,10 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}), flush=True)
         sys.exit(2)
+    BUSY["on"] = args.busy_segments
+    if args.floor_driver:
+        print(json.dumps(launch_floor(args)), flush=True)
+        return
     if args.pmc_driver:
         pmc_driver()
         return

@@ -105,7 +105,10 @@ struct MoeTokArgs {
   int32_t* ids;                                     // [m][top_k], rank order
   float* w;                                         // [m][top_k]
   float* g;                                         // [m] (written when there is a shared expert)
-  float* h;                                         // fp32 [m][top_k + 1][inter]
+  float* h;                                         // fp32 h rows, see inv
+  const int32_t* inv;                               // null: h row of (t, d) is t (top_k + 1) + d;
+                                                    // else inv[t top_k + d], and m top_k + t for
+                                                    // the shared expert (the grouped kernels' rows)
   float* y;                                         // fp32 [m][hidden]
 };
 // Largest batch the per-token path takes (beyond it the grouped kernels read each selected
@@ -114,5 +117,8 @@ constexpr int kTokPathMaxM = 4;
 // Whether the per-token kernels take this call (the down kernel stages every slot's h row).
 bool moe_tok_supported(int m, int top_k, int inter);
 hipError_t moe_tok_launch(const MoeTokArgs& a, hipStream_t s);
+// The per-token down + combine kernel alone, on h rows written by the grouped gate/up kernel
+// (a.inv set): the grouped path's last two launches in one (m <= 32, inter <= 2048).
+hipError_t moe_tok_down_launch(const MoeTokArgs& a, hipStream_t s);
 
 }  // namespace bfp

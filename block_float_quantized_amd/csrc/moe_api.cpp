@@ -167,6 +167,11 @@ int32_t check_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, cons
   return BFP_OK;
 }
 
+// Largest batch whose grouped path ends with the per-token down + combine kernel: it reads
+// an expert's down rows once per (token, slot) instead of once per expert, which costs more
+// than the combine launch it saves once experts are shared by many tokens.
+constexpr int kTokDownMaxM = 8;
+
 // The layer's kernels on a checked call; ws holds at least layout(L, m, true).total bytes.
 int32_t moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, float* y, int32_t* topk_ids,
                     float* topk_w, void* ws, hipStream_t s) {
@@ -241,6 +246,17 @@ int32_t moe_forward(const bfp_moe_layer* L, const uint16_t* x, int64_t m, float*
   gu.tile_start = d.tile_start; gu.tile_m = d.tile_m;
   if ((e = bfp::moe_gemv_launch(gu, 2, s)) != hipSuccess) return BFP_E_DEVICE;
 
+  if (m <= kTokDownMaxM && L->inter <= 2048) {
+    // down projection and combine per token (the combine's order, one launch fewer)
+    bfp::MoeTokArgs a{};
+    a.m = (int)m; a.n_exp = L->n_experts; a.top_k = L->top_k;
+    a.hidden = (int)L->hidden; a.inter = (int)L->inter;
+    a.d_exp = L->down.exp; a.d_code = L->down.code;
+    if (shared) { a.sd_exp = L->sh_down.exp; a.sd_code = L->sh_down.code; }
+    a.ids = ids; a.w = w; a.g = g;
+    a.h = h; a.inv = d.inv; a.y = y;
+    return from_hip(bfp::moe_tok_down_launch(a, s));
+  }
   bfp::MoeGemvArgs dn = gu;
   dn.exp0 = L->down.exp; dn.code0 = L->down.code; dn.exp1 = nullptr; dn.code1 = nullptr;
   dn.sexp0 = shared ? L->sh_down.exp : nullptr; dn.scode0 = shared ? L->sh_down.code : nullptr;

@@ -253,10 +253,13 @@ __global__ __launch_bounds__(kWave * 9) void tok_down_kernel(MoeTokArgs ma) {
   load_group<4, BPU, 2, 1, 1, LPR>(ga, codem, expm, rowc, ma.inter, nbk, 0, 0, p, nuc);
   if (ng > 1) load_group<4, BPU, 2, 1, 1, LPR>(gb, codem, expm, rowc, ma.inter, nbk, 0, STEP, p, nuc);
   const int per_row = ma.inter / 4;
-  const float* ht = ma.h + (int64_t)t * ns * ma.inter;
+  auto hrow = [&](int dd) -> int64_t {
+    if (!ma.inv) return (int64_t)t * ns + dd;
+    return dd < ma.top_k ? ma.inv[(int64_t)t * ma.top_k + dd] : (int64_t)ma.m * ma.top_k + t;
+  };
   for (int idx = threadIdx.x; idx < ns * per_row; idx += blockDim.x) {
     const int mi = idx / per_row, c4 = idx % per_row;
-    const uint4 v = *reinterpret_cast<const uint4*>(ht + (int64_t)mi * ma.inter + c4 * 4);
+    const uint4 v = *reinterpret_cast<const uint4*>(ma.h + hrow(mi) * ma.inter + c4 * 4);
     const int kk = c4 * 4;
     *reinterpret_cast<uint4*>(xs + ((size_t)mi * nuc + kk / 32) * L::kStrideDw + (kk % 32)) = v;
   }
@@ -308,6 +311,16 @@ hipError_t tok_down(const MoeTokArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t moe_tok_down_launch(const MoeTokArgs& a, hipStream_t s) {
+  if (a.m < 1 || a.m > 32 || a.top_k < 1 || a.top_k > 8 || a.inter % 32 != 0 || a.inter > 2048)
+    return hipErrorInvalidValue;
+  switch (moe_lpr(a.inter)) {
+    case 4: return tok_down<4>(a, s);
+    case 8: return tok_down<8>(a, s);
+    default: return tok_down<16>(a, s);
+  }
+}
 
 bool moe_tok_supported(int m, int top_k, int inter) {
   // the down kernel's LDS: every slot's h row, 144 bytes per 32 values (at most 83 KB)

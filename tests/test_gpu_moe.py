@@ -85,7 +85,7 @@ def moe_full():
     return layer, dev, LazyBank(layer)
 
 
-@pytest.mark.parametrize("m", [1, 8, 16])
+@pytest.mark.parametrize("m", [1, 3, 8, 16])
 def test_moe_decode_matches_oracle(moe_full, m):
     layer, dev, bank = moe_full
     note(f"moe decode m={m}")
@@ -258,7 +258,7 @@ _ONE_TOKEN_SHAPES = [(16, 4, 256, 96, True), (32, 8, 1024, 640, False), (4, 2, 2
 @pytest.mark.parametrize("n_exp,top_k,hidden,inter,shared", _ONE_TOKEN_SHAPES)
 def test_moe_one_token_shapes(n_exp, top_k, hidden, inter, shared):
     """One token against the oracle (ids, weights, gate, y), and the same bits as that token's
-    row of a 3-token call (the grouped expert kernels)."""
+    row of a 3-token call (per-token kernels) and of a 6-token call (grouped kernels)."""
     note(f"moe one token E={n_exp} k={top_k} H={hidden} F={inter} shared={shared}")
     layer = _small_layer(50 + top_k, n_exp=n_exp, hidden=hidden, inter=inter, top_k=top_k)
     if not shared:
@@ -266,7 +266,7 @@ def test_moe_one_token_shapes(n_exp, top_k, hidden, inter, shared):
             layer[name] = np.zeros_like(layer[name])
     dev = device_layer(layer, shared=shared)
     rng = np.random.default_rng(51)
-    x = synth.bf16_bits(rng.standard_normal((3, hidden)).astype(np.float32))
+    x = synth.bf16_bits(rng.standard_normal((6, hidden)).astype(np.float32))
     xd = dev_bf16(x)
     ids = torch.empty((1, top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((1, top_k), dtype=torch.float32, device="cuda")
@@ -278,8 +278,10 @@ def test_moe_one_token_shapes(n_exp, top_k, hidden, inter, shared):
         rt["g"] = np.zeros(1)              # no shared term (its weights are zero as well)
     ref, norm = oracle.moe_decode(LazyBank(layer), x[1:2], rt)
     assert_within(y1.cpu().numpy(), ref, norm, TOL, what="moe one token")
-    y3 = bfq.bfp_moe_forward(dev, xd)
+    y3 = bfq.bfp_moe_forward(dev, xd[:3].contiguous())
     assert torch.equal(y1.view(torch.int32), y3[1:2].view(torch.int32))
+    y6 = bfq.bfp_moe_forward(dev, xd)
+    assert torch.equal(y1.view(torch.int32), y6[1:2].view(torch.int32))
 
 
 @pytest.mark.parametrize("m", [4, 40])
