@@ -52,12 +52,6 @@ def bf16_round(v: np.ndarray) -> np.ndarray:
     return out
 
 
-def bf16_bits_of(v: np.ndarray) -> np.ndarray:
-    """Bit patterns of values that are already bf16-representable (fp64 input)."""
-    f = np.asarray(v, dtype=np.float64).astype(np.float32)
-    return (f.view(np.uint32) >> 16).astype(np.uint16)
-
-
 def gemm(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     """y[m][n] = sum_k x[m][k] * w[n][k] in fp64 (x [M][K], w [N][K], both fp64 values)."""
     x = np.asarray(x, dtype=np.float64)

@@ -154,6 +154,23 @@ def test_sigmoid_pins():
     assert np.all(np.diff(v) > 0) and np.all(v[z > 0] > 0.5) and np.all(v[z < 0] < 0.5)
 
 
+def test_normaliser_hand_case():
+    """sum_k |x_ik| |w_jk|, worked by hand."""
+    x = np.array([[1.0, -2.0], [0.5, 0.0]])
+    w = np.array([[3.0, 4.0], [-1.0, 0.5]])
+    assert np.array_equal(oracle.normaliser(x, w), np.array([[11.0, 2.0], [1.5, 0.5]]))
+
+
+def test_bf16_to_f64_known_patterns():
+    """bf16 bit patterns with known values: 1, -2, the smallest subnormal 2^-133, the largest
+    finite (2 - 2^-7) 2^127, +inf, -0."""
+    bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0x7F80, 0x8000], dtype=np.uint16)
+    v = oracle.bf16_to_f64(bits)
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 2.0 ** -133
+    assert v[3] == (2.0 - 2.0 ** -7) * 2.0 ** 127 and math.isinf(v[4]) and v[4] > 0
+    assert v[5] == 0.0 and math.copysign(1.0, v[5]) < 0
+
+
 def test_rel_err_zero_normaliser():
     r = oracle.rel_err(np.array([0.0, 1.0, 2.0]), np.array([0.0, 0.5, 2.0]), np.array([0.0, 0.0, 4.0]))
     assert r[0] == 0.0 and math.isinf(r[1]) and r[2] == 0.0
