@@ -61,7 +61,8 @@ template <> struct BlockCodes<4> { using T = u32x2; };    // 16 nibbles
 template <> struct BlockCodes<8> { using T = u32x4; };    // 16 bytes
 
 // Batch size and ring depth from the task shape (tasks of two matrices are five times the bytes
-// of one-step tasks).
+// of one-step tasks). A one-matrix launch whose workgroups would have fewer batches than waves
+// (a short matrix) uses one row per batch instead.
 template <int NMAT, int J> constexpr int kBatch = NMAT == 2 ? 1 : (J >= 3 ? 2 : 4);
 template <int NMAT, int J> constexpr int kDepth = (NMAT == 1 && J == 1) ? 3 : 2;
 
@@ -245,9 +246,8 @@ __device__ __forceinline__ void reduce_store(float (&v)[B * NMAT], const BatchPo
   }
 }
 
-template <int FMT, int NMAT, bool XB, int J, bool AM>
+template <int FMT, int NMAT, bool XB, int J, bool AM, int B = kBatch<NMAT, J>>
 __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
-  constexpr int B = kBatch<NMAT, J>;
   constexpr int D = kDepth<NMAT, J>;
   using BatchT = Batch<FMT, NMAT, J, B>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -396,6 +396,13 @@ hipError_t launch_j(RowArgs a, hipStream_t s) {
   size_t lds = lds_bytes(a.k, XB, a.rows, a.slices, NMAT);
   if (lds > kLdsMax) return hipErrorNotSupported;
   if (lds < kLdsFloor) lds = kLdsFloor;
+  if constexpr (NMAT == 1 && !AM && kBatch<NMAT, J> > 1) {
+    // few tasks per workgroup (a short matrix): one row per batch, so that every wave has one
+    if ((a.rows * a.slices + kBatch<NMAT, J> - 1) / kBatch<NMAT, J> < kWaves) {
+      hipLaunchKernelGGL((row_gemv_kernel<FMT, NMAT, XB, J, AM, 1>), dim3(grid), dim3(kThreads), lds, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((row_gemv_kernel<FMT, NMAT, XB, J, AM>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
