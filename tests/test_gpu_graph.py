@@ -32,6 +32,9 @@ def test_graph_replay_matches_eager_calls():
     xm = dev_bf16(synth.moe_tokens(4, 0))
     ym = torch.empty((4, 2048), dtype=torch.float32, device="cuda")
     ws_m = torch.empty((bfq.bfp_moe_workspace_bytes(layer, 4),), dtype=torch.uint8, device="cuda")
+    xm8 = dev_bf16(synth.moe_tokens(8, 1))              # grouped gate/up, per-token down
+    ym8 = torch.empty((8, 2048), dtype=torch.float32, device="cuda")
+    ws_m8 = torch.empty((bfq.bfp_moe_workspace_bytes(layer, 8),), dtype=torch.uint8, device="cuda")
 
     kvh, hd, L = 2, 256, 3000
     cache = bfq.KvCache.empty(kvh, hd, L, v_format=bfq.KV_V_BFP4_HADAMARD)
@@ -45,9 +48,10 @@ def test_graph_replay_matches_eager_calls():
         bfq.bfp_gemm(g, x, w_up=u, out=h, workspace=ws_gu)
         bfq.bfp_gemm(d, h, out=y, workspace=ws_d)
         bfq.bfp_moe_forward(layer, xm, out=ym, workspace=ws_m)
+        bfq.bfp_moe_forward(layer, xm8, out=ym8, workspace=ws_m8)
         bfq.bfp_attn_decode(cache, q, L, 1.0 / 16, out=ya, workspace=ws_a)
 
-    outs = [h, y, ym, ya]
+    outs = [h, y, ym, ym8, ya]
     calls()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]

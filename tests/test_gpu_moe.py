@@ -250,9 +250,10 @@ def test_moe_decode_extreme_exponents(m):
 
 # (experts, top_k, hidden, inter, shared): lanes per row 4 / 8 / 16 in the gate/up and down
 # kernels, a half-filled last row tile (inter 96), a one-unit second group (inter 1056), no
-# shared expert, top-1, and an intermediate size past the one-token kernels' limit (2080)
+# shared expert, top-1, an intermediate size past the per-token kernels' limit (2080), and
+# the largest one they take with nine slots (83 KB of staged h per down workgroup)
 _ONE_TOKEN_SHAPES = [(16, 4, 256, 96, True), (32, 8, 1024, 640, False), (4, 2, 2080, 1056, True),
-                     (8, 1, 128, 2080, True), (6, 3, 512, 512, False)]
+                     (8, 1, 128, 2080, True), (6, 3, 512, 512, False), (8, 8, 256, 2048, True)]
 
 
 @pytest.mark.parametrize("n_exp,top_k,hidden,inter,shared", _ONE_TOKEN_SHAPES)

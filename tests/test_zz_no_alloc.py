@@ -28,7 +28,8 @@ def _reference(dev, x):
 
 
 def test_noalloc_matches_workspace_call_twice(layer_dev):
-    for m, seed in ((16, 40), (3, 41)):
+    # 16 tokens: grouped kernels; 8: grouped gate/up, per-token down; 3: per-token kernels
+    for m, seed in ((16, 40), (8, 42), (3, 41)):
         note(f"no-alloc moe decode m={m}")
         x = dev_bf16(synth.moe_tokens(m, seed))
         y_ref, ids_ref, w_ref = _reference(layer_dev, x)
