@@ -81,8 +81,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_bfp4_gateup_m1_hbm_traffic.m
 # the headline kernel's translation unit and every header it includes
 HEADLINE_SOURCES = tuple(f"block_float_quantized_amd/csrc/{f}" for f in (
     "gemv_b4_bf16x.hip", "gemv_row.hpp", "gemv_impl.hpp", "bfp_device.hpp", "bfp_internal.hpp", "argmax.hpp"))
-HEADLINE_KERNEL = "row_gemv_kernel<4, 2, true, 5, false>"
-DOWN_KERNEL = "row_gemv_kernel<4, 1, false, 1, false>"     # the step's down projection
+HEADLINE_KERNEL = "row_gemv_kernel<4, 2, true, 5, false, 1>"
+DOWN_KERNEL = "row_gemv_kernel<4, 1, false, 1, false, 4>"     # the step's down projection
 COPY_BYTES = 512 << 20
 
 
