@@ -64,6 +64,13 @@ def parse():
                     help="only time the MoE workloads (decode and the 2,048-token prefill) and print their lines")
     ap.add_argument("--kernel-summary", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace output folder into a per-kernel markdown table")
+    ap.add_argument("--counter-driver", action="store_true",
+                    help="only launch the decode workloads (16 calls each over cold replicas, between marker "
+                         "kernels) and a 512 MiB copy, for rocprofv3 --pmc passes")
+    ap.add_argument("--counter-report", nargs="+", metavar="PMC_DIR",
+                    help="turn rocprofv3 --pmc folders of --counter-driver (any counters among FETCH_SIZE, "
+                         "WRITE_SIZE, TCC_HIT_sum, TCC_MISS_sum, SQ_INSTS_VALU, GRBM_GUI_ACTIVE) into a "
+                         "per-workload, per-kernel table")
     ap.add_argument("--floor-driver", action="store_true",
                     help="only time the launch floor: a one-element fill kernel, eager and graph-replayed")
     ap.add_argument("--busy-segments", action="store_true",
@@ -615,6 +622,132 @@ def cpu_baseline(c: dict, xbits: np.ndarray) -> dict:
             "per_config": out}
 
 
+# ---- decode counters ------------------------------------------------------------------------
+
+COUNTER_CALLS = 16
+
+
+def counter_driver():
+    """The decode workloads one after the other, each as COUNTER_CALLS calls over cold weight
+    replicas between two marker kernels, then a plain copy of COPY_BYTES (the byte counters'
+    calibration). The marker order is the order of `names` (logged)."""
+    import torch
+    import block_float_quantized_amd as bfq
+    import synth
+    torch.cuda.set_device(0)
+
+    def segment(name, fn):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(1000)
+        for i in range(COUNTER_CALLS):
+            fn(i)
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        log(f"counter segment: {name}")
+
+    c, mats = make_mlp(8)
+    x = bf16_dev(c["x"])
+    h = torch.empty((1, INTER), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, HIDDEN), dtype=torch.bfloat16, device="cuda")
+    segment("dense BFP4 MLP M=1", lambda i: (bfq.bfp_gemm(mats[i % 8][0], x, w_up=mats[i % 8][1], out=h),
+                                             bfq.bfp_gemm(mats[i % 8][2], h, out_dtype=torch.bfloat16, out=y)))
+    del mats, c
+    torch.cuda.empty_cache()
+    g = synth.gemv_case(0)
+    p1 = synth.proj_case(1, 0, with_lm=False)
+    for name, w, xb in (("BFP8 GEMV 2048x2048 M=1", g["w"], g["x"]), ("BFP8 QKV 2048->5120 M=1", p1["wqkv"], p1["x"]),
+                        ("BFP8 O 4096->2048 M=1", p1["wo"], p1["xo"]),
+                        ("BFP8 LM head 2048->151936 M=1", synth.dense_weights(0, 3, "lm", 151936, 2048, 0.02), p1["x"])):
+        base = quantize(8, w)
+        R = replicas_for(base.nbytes)
+        reps = [base] + [clone(base) for _ in range(R - 1)]
+        xx = bf16_dev(xb)
+        yy = torch.empty((1, base.n), dtype=torch.float32, device="cuda")
+        ws = workspace(bfq.bfp_gemm_workspace_bytes(base, 1))
+        segment(name, lambda i: bfq.bfp_gemm(reps[i % R], xx, out=yy, workspace=ws))
+        del reps, base
+        torch.cuda.empty_cache()
+    layer = synth.moe_layer(0)
+    q = {k: quantize(4, layer[k]) for k in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")}
+    layers = []
+    for r in range(4):
+        qq = q if r == 0 else {k: clone(v) for k, v in q.items()}
+        layers.append(bfq.MoeLayer(256, 8, 2048, 512, bf16_dev(layer["router"]), None, qq["gate"], qq["up"],
+                                   qq["down"], qq["sh_gate"], qq["sh_up"], qq["sh_down"], bf16_dev(layer["sh_gate_w"])))
+    xs = [bf16_dev(synth.moe_tokens(1, s_)) for s_ in range(8)]
+    ym = torch.empty((1, 2048), dtype=torch.float32, device="cuda")
+    wsm = torch.empty((bfq.bfp_moe_workspace_bytes(layers[0], 1),), dtype=torch.uint8, device="cuda")
+    segment("moe decode M=1", lambda i: bfq.bfp_moe_forward(layers[i % 4], xs[i % 8], out=ym, workspace=wsm))
+    del layers, q
+    torch.cuda.empty_cache()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log("counter driver done")
+
+
+def counter_report(dirs):
+    """Per workload (segments between marker kernels, in the driver's order) and kernel: the
+    mean per dispatch of each counter collected; bytes calibrated by the copy (FETCH_SIZE and
+    WRITE_SIZE in KiB), L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS), VALU issue = 4 cycles per
+    wave64 VALU instruction per SIMD (1024) over the GPU cycles (GRBM_GUI_ACTIVE / 8 XCDs)."""
+    import glob
+    import sqlite3
+    names = ["dense BFP4 MLP M=1", "BFP8 GEMV 2048x2048 M=1", "BFP8 QKV 2048->5120 M=1", "BFP8 O 4096->2048 M=1",
+             "BFP8 LM head 2048->151936 M=1", "moe decode M=1"]
+    vals = {}        # (segment, kernel) -> counter -> [values]
+    dur = {}
+    copy = {}
+    for d in dirs:
+        db = glob.glob(os.path.join(d, "**", "*.db"), recursive=True)[0]
+        rows = sqlite3.connect(db).execute(
+            "select dispatch_id, kernel_name, counter_name, value, duration from counters_collection "
+            "order by dispatch_id").fetchall()
+        seg, inside, last = -1, False, None
+        for did, kname, cn, v, du in rows:
+            if MARKER_KERNEL in kname:
+                if did != last:
+                    inside = not inside
+                    if inside:
+                        seg += 1
+                last = did
+                continue
+            last = did
+            if "MulFunctor" in kname:
+                copy.setdefault(cn, []).append(v)
+                continue
+            if not inside or seg >= len(names):
+                continue
+            key = (names[seg], short_kernel_name(kname))
+            vals.setdefault(key, {}).setdefault(cn, []).append(v)
+            dur.setdefault(key, {})[did] = du
+    mean = lambda a: sum(a) / len(a)
+    kib = COPY_BYTES / 1024
+    ff = kib / mean(copy["FETCH_SIZE"]) if "FETCH_SIZE" in copy else None
+    fw = kib / mean(copy["WRITE_SIZE"]) if "WRITE_SIZE" in copy else None
+    print("| workload | kernel | dispatches | avg (us) | HBM read MB | HBM written MB | L2 hit | VALU issue |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|")
+    for (wl, k), cs in vals.items():
+        n = len(dur[(wl, k)])
+        us = mean(list(dur[(wl, k)].values())) / 1000.0
+        rd = f"{mean(cs['FETCH_SIZE']) * 1024 * ff / 1e6:.2f}" if "FETCH_SIZE" in cs and ff else ""
+        wr = f"{mean(cs['WRITE_SIZE']) * 1024 * fw / 1e6:.3f}" if "WRITE_SIZE" in cs and fw else ""
+        hit = ""
+        if "TCC_HIT_sum" in cs and "TCC_MISS_sum" in cs:
+            h_, m_ = mean(cs["TCC_HIT_sum"]), mean(cs["TCC_MISS_sum"])
+            hit = f"{100 * h_ / max(h_ + m_, 1):.0f}%"
+        valu = ""
+        if "SQ_INSTS_VALU" in cs and "GRBM_GUI_ACTIVE" in cs:
+            cyc = mean(cs["GRBM_GUI_ACTIVE"]) / 8
+            valu = f"{100 * mean(cs['SQ_INSTS_VALU']) * 4 / 1024 / max(cyc, 1):.0f}%"
+        print(f"| {wl} | `{k}` | {n} | {us:.2f} | {rd} | {wr} | {hit} | {valu} |")
+    if ff and fw:
+        print(f"\ncalibration: the copy reads and writes {kib:.0f} KiB per dispatch; FETCH_SIZE factor {ff:.4f}, "
+              f"WRITE_SIZE factor {fw:.4f}")
+
+
 # ---- other workloads -----------------------------------------------------------------------
 
 def launch_floor(args):
@@ -795,6 +928,9 @@ def main():
     if args.pmc_report:
         pmc_report(*args.pmc_report)
         return
+    if args.counter_report:
+        counter_report(args.counter_report)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}), flush=True)
         sys.exit(2)
@@ -804,6 +940,9 @@ def main():
         return
     if args.pmc_driver:
         pmc_driver()
+        return
+    if args.counter_driver:
+        counter_driver()
         return
     if args.attn_driver:
         print(json.dumps(attn_workloads(args)), flush=True)
