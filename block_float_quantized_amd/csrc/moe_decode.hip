@@ -7,6 +7,11 @@
 // tile as the dense GEMV, for all (token, slot) pairs routed to it; the shared expert is one
 // more group with every token. The combine then forms y_t = sum_j w_tj o_tj (slots in rank
 // order) + g_t * shared_t, a fixed order, so the result does not depend on scheduling.
+//
+// For a few tokens the same tiles run per (token, slot) instead (the per-token path below):
+// every gate/up workgroup ranks its token's experts itself, and the down kernel combines each
+// token's slots in the same order, so no dispatch, per-pair outputs or combine launch remain.
+// Both paths give each token the same bits.
 #include "bfp_moe.hpp"
 #include "gemv_impl.hpp"
 #include "moe_topk.hpp"

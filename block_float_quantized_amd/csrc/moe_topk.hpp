@@ -1,6 +1,6 @@
 #pragma once
 // Top-k routing of one token on one wave (gfx950), shared by the routing kernels and the
-// one-token decode kernels.
+// per-token decode kernels.
 //
 // "Qwen3.6-35B-A3B — TT-native mixed BFP4/BFP8 (GPTQ experts)", sections "Precision as served"
 // (BF16 router) and "Fused decode kernels" (device top-k routing): the experts are ranked by
