@@ -14,8 +14,12 @@ before timing. Packed weights are replicated (or several layers are built) so co
 calls read different copies, >= 1 GiB apart in total (more than four times the 256 MB
 last-level cache): the bandwidths are HBM numbers. Each timed loop runs W warm-up calls, then
 K calls between two events on the launch stream. The headline step is timed as a decode loop
-launches it, from a HIP graph holding one step per weight replica (K steps = K / 8 replays,
-after replays checked bit for bit against eager steps); its eager time is reported beside it. Bandwidth = algorithmic bytes (packed
+launches it: the K steps (consecutive steps read the weight replicas in turn) captured as one
+HIP graph, checked bit for bit against eager steps and replayed once after the W warm-up steps
+(another graph's replay). Before the headline's measurements the step runs back to back,
+untimed, for --clock-ramp-ms, so that the GPU clocks have left their idle levels, as in a
+decode loop that runs without pause; the same graph measurement taken before that ramp, and
+the eager time, are reported beside it. Bandwidth = algorithmic bytes (packed
 weights actually read + activations in + outputs out) / time per call. The dominant kernel
 of the headline step (gate/up + SwiGLU GEMV) is timed alone over K back-to-back launches for
 the roofline entry. The CPU oracle is timed on the host: the headline step whole, and one
@@ -50,6 +54,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--clock-ramp-ms", type=float, default=300.0,
+                    help="untimed: run the headline step back to back for this long before its "
+                         "measurements, so that the GPU clocks are at their working level (0: off)")
     ap.add_argument("--M", type=int, default=1)
     ap.add_argument("--quick", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -365,17 +372,16 @@ def timed_graph(fn, outs, calls: int = 64, reps: int = 10):
         return None
 
 
-def graph_steps(fn, outs, period: int, steps: int, warmup: int):
-    """ms per step over exactly `steps` steps (rounded up to a multiple of `period`) launched from
-    one HIP graph holding `period` consecutive steps fn(0), ..., fn(period - 1) (one per weight
-    replica), replayed after `warmup` steps' worth of replays. First, three replays (each after
-    eager work that zeroes the outputs, and a synchronisation) must leave every tensor in `outs`
-    bit-identical to an eager run of the same steps; else (or if capture fails) None. Returns
-    (ms per step, steps timed)."""
+def graph_steps(fn, outs, steps: int, warmup: int):
+    """ms per step over exactly `steps` consecutive steps fn(0), ..., fn(steps - 1) launched as one
+    HIP graph replay, after `warmup` steps fn(0), ..., fn(warmup - 1) launched as the replay of a
+    second graph (untimed). First, three replays of the timed graph (each after eager work that
+    zeroes the outputs, and a synchronisation) must leave every tensor in `outs` bit-identical
+    to an eager run of the same steps; else (or if capture fails) None. Returns ms per step."""
     import torch
     try:
         torch.cuda.synchronize()
-        for i in range(period):
+        for i in range(steps):
             fn(i)
         torch.cuda.synchronize()
         ref = [o.clone() for o in outs]
@@ -384,38 +390,56 @@ def graph_steps(fn, outs, period: int, steps: int, warmup: int):
         with torch.cuda.stream(side):
             fn(0)
         torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(period):
-                fn(i)
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    fn(i)
+            return g
+
+        gk = capture(steps)
+        gw = capture(warmup) if warmup > 0 else None
         for _ in range(3):
             for o in outs:
                 o.zero_()
             torch.cuda.synchronize()
-            g.replay()
+            gk.replay()
             torch.cuda.synchronize()
             for o, r in zip(outs, ref):
                 if not torch.equal(o.view(torch.uint8), r.view(torch.uint8)):
                     log("graph replay differs from the eager steps; graph timing skipped")
                     return None
-        reps = -(-steps // period)
-        for _ in range(-(-warmup // period)):
-            g.replay()
+        if gw is not None:
+            gw.replay()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        for _ in range(reps):
-            g.replay()
+        gk.replay()
         t1.record(stream)
         torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / (reps * period)
-        del g
-        return ms, reps * period
+        ms = t0.elapsed_time(t1) / steps
+        del gk, gw
+        return ms
     except RuntimeError as e:
         log(f"graph timing skipped: {e}")
         return None
+
+
+def clock_ramp(fn, ms: float) -> int:
+    """Untimed: calls fn(i) back to back for `ms` milliseconds of wall time (synchronising every
+    32 calls), so that the GPU's core and memory clocks leave their idle states before a
+    measurement, as in a decode loop that runs without pause. Returns the calls made."""
+    import torch
+    n, t = 0, time.perf_counter()
+    while (time.perf_counter() - t) * 1e3 < ms:
+        for _ in range(32):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def add_graph_timing(entry: dict, fn, outs, nbytes: int):
@@ -469,6 +493,11 @@ def run_mlp(args, m, mats, xb, batch_invariant=False, graph=False):
         g, u, _ = mats[i % R]
         bfq.bfp_gemm(g, x, w_up=u, out=h, workspace=ws_gu, batch_invariant=batch_invariant)
 
+    cold = None
+    if graph and args.clock_ramp_ms > 0:
+        # the same measurement without the ramp, for reference
+        cold = graph_steps(step, [h, y], args.steps, args.warmup)
+        ramp_calls = clock_ramp(step, args.clock_ramp_ms)
     ms_step = timed(step, args.steps, args.warmup)
     ms_gu = timed(gateup, args.steps, args.warmup)
     busy_segment(f"dense BFP4 MLP M={m}" + (" batch-invariant" if batch_invariant else ""), step)
@@ -478,12 +507,12 @@ def run_mlp(args, m, mats, xb, batch_invariant=False, graph=False):
            "bytes": b["step"], "tok_per_s": m / (ms_step * 1e-3)}
     if graph:
         # the step as a decode loop launches it: from a HIP graph (eager above for reference)
-        r = graph_steps(step, [h, y], R, args.steps, args.warmup)
-        if r is not None:
-            ms_g, n = r
+        ms_g = graph_steps(step, [h, y], args.steps, args.warmup)
+        if ms_g is not None:
             out.update({"us_per_step_eager": ms_step * 1e3, "us_per_call": ms_g * 1e3,
-                        "GB/s": b["step"] / (ms_g * 1e-3) / 1e9, "tok_per_s": m / (ms_g * 1e-3),
-                        "graph_steps_timed": n})
+                        "GB/s": b["step"] / (ms_g * 1e-3) / 1e9, "tok_per_s": m / (ms_g * 1e-3)})
+        if cold is not None:
+            out.update({"us_per_step_graph_no_ramp": cold * 1e3, "clock_ramp_calls": ramp_calls})
     return out
 
 
@@ -995,13 +1024,17 @@ def main():
         "value": round(head["GB/s"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": head.get("graph_steps_timed", args.steps),
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(head["us_per_call"] * 1e-3, 5),
         "us_per_call": round(head["us_per_call"], 2),
         "us_per_step_eager": round(head["us_per_step_eager"], 2) if "us_per_step_eager" in head else None,
-        "timing": "HIP graph of one step per weight replica, replayed" if "us_per_step_eager" in head
-                  else "eager launches",
+        "us_per_step_graph_no_ramp": round(head["us_per_step_graph_no_ramp"], 2)
+                                     if "us_per_step_graph_no_ramp" in head else None,
+        "clock_ramp_ms": args.clock_ramp_ms,
+        "timing": ("the K steps (weight replicas in turn) as one HIP graph replay, after the W warmup steps "
+                   "as another; before both, the step run back to back for clock_ramp_ms (untimed)")
+                  if "us_per_step_eager" in head else "eager launches",
         "pct_hbm_peak": round(100 * head["GB/s"] / HBM_PEAK_GBS, 1),
         "higher_is_better": True,
         "scaling": "weak",
