@@ -19,11 +19,13 @@
 //    The workgroup stages x in LDS once; a wave keeps its lanes' x values of the current slice
 //    in registers (bf16 pairs in the unpack's pair order, or fp32), so no weight is ever
 //    matched against x read back from LDS.
-//  * A workgroup's tasks are cut into batches of B rows of one slice, the batches spread evenly
-//    over the waves (consecutive batches per wave, slice by slice); each wave keeps the loads of
-//    the next D - 1 batches in flight while it computes one (a ring of register buffers, loaded
-//    without branches except in the wave's last round, so that the compiler's wait counts stay
-//    exact; the rows of a short batch are clamped to its last row).
+//  * A workgroup's tasks are cut into batches of B rows of one slice (slice by slice), handed to
+//    the waves in order from a counter in LDS as they ask for them (the waves sharing a SIMD
+//    do not progress evenly; with a fixed share each, the compute unit would run the end of
+//    the call with fewer loads in flight); each wave keeps the loads of the next D - 1 batches
+//    in flight while it computes one (a ring of register buffers, loaded without branches, so
+//    that the compiler's wait counts stay exact; the rows of a short batch are clamped to its
+//    last row).
 //  * A batch's B x NMAT lane sums are reduced over the 64 lanes by recursive halving
 //    (v_permlane32_swap, v_permlane16_swap, then DPP), the same tree (lane pairs at distance
 //    32, 16, ..., 1) for every value; the results go to LDS as partials[row][slice][matrix].
@@ -261,16 +263,21 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
   const int nr = min(a.rows, a.n - row0);
   const int nbs = (nr + B - 1) / B;                  // batches per slice
   const int nb = nbs * a.slices;
-  const int b_beg = (int)((int64_t)wave * nb / kWaves);
-  const int b_end = (int)((int64_t)(wave + 1) * nb / kWaves);
 
-  // the first batches' loads are in flight while x is staged (a wave with fewer batches re-reads
-  // its last one: no branch, so that the wait counts stay exact)
+  // Batches are handed out in order from a workgroup counter in LDS, so a wave that runs ahead
+  // (the three waves of a SIMD progress unevenly) takes more of them and all waves finish
+  // together. The first D - 1 batches of each wave are dealt round-robin (index wave +
+  // kWaves d) and loaded while x is staged; an index past the last batch loads the last one
+  // (no branch, so that the wait counts stay exact) and is never computed.
+  __shared__ int next_batch;
   BatchT ring[D];
-  const int b_last = max(b_end - 1, 0);
+  int idx[D];
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d)
-    load_batch<FMT, NMAT, J, B>(ring[d], a, row0, batch_pos(min(b_beg + d, b_last), nbs, nr, B), lane);
+  for (int d = 0; d < D - 1; ++d) {
+    idx[d] = wave + kWaves * d;
+    load_batch<FMT, NMAT, J, B>(ring[d], a, row0, batch_pos(min(idx[d], nb - 1), nbs, nr, B), lane);
+  }
+  if (threadIdx.x == 0) next_batch = kWaves * (D - 1);
   {
     const int n16 = a.k * (XB ? 2 : 4) / 16;
     const uint4* src = static_cast<const uint4*>(a.x);
@@ -287,33 +294,44 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
       cur = p.s;
     }
   };
-  int bi = b_beg;
-  // steady state: every load of the round is in range, none is conditional
-  for (; bi + 2 * D - 2 < b_end; bi += D) {
+  auto take = [&]() -> int {                          // the next batch index, the same in every lane
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next_batch, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  // Steady state: slot d holds a loaded batch; the next index is taken and, while it is a
+  // batch, its loads go into the free slot as slot d is computed (no load is conditional on
+  // this path). Indices only grow, so once one is past the end the wave computes the D - 1
+  // slots still in flight that hold a batch, in order, and stops.
+  bool live = true;
+  while (live) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const BatchPos p = batch_pos(bi + d, nbs, nr, B);
+      if (!live) break;
+      const int nxt = take();
+      if (nxt >= nb) {
+#pragma unroll
+        for (int e = 0; e < D - 1; ++e) {
+          const int sl = (d + e) % D;
+          if (idx[sl] < nb) {
+            const BatchPos p = batch_pos(idx[sl], nbs, nr, B);
+            x_for(p);
+            float v[B * NMAT];
+            sum_batch<FMT, NMAT, XB, J, B>(ring[sl], xr, v);
+            reduce_store<NMAT, B>(v, p, part, a.slices, lane);
+          }
+        }
+        live = false;
+        break;
+      }
+      // here idx[d] < nb too: every index dealt before nxt is smaller than it
+      const BatchPos p = batch_pos(idx[d], nbs, nr, B);
       x_for(p);
       float v[B * NMAT];
-      load_and_sum<FMT, NMAT, XB, J, B>(ring[(d + D - 1) % D], a, row0, batch_pos(bi + d + D - 1, nbs, nr, B),
-                                        ring[d], xr, v, lane);
+      load_and_sum<FMT, NMAT, XB, J, B>(ring[(d + D - 1) % D], a, row0, batch_pos(nxt, nbs, nr, B), ring[d], xr,
+                                        v, lane);
       reduce_store<NMAT, B>(v, p, part, a.slices, lane);
-    }
-  }
-  // last rounds (at most 2 D - 2 batches are left): batches past the wave's range are neither
-  // loaded nor computed (wave-uniform conditions)
-  for (; bi < b_end; bi += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (bi + d + D - 1 < b_end)
-        load_batch<FMT, NMAT, J, B>(ring[(d + D - 1) % D], a, row0, batch_pos(bi + d + D - 1, nbs, nr, B), lane);
-      if (bi + d < b_end) {
-        const BatchPos p = batch_pos(bi + d, nbs, nr, B);
-        x_for(p);
-        float v[B * NMAT];
-        sum_batch<FMT, NMAT, XB, J, B>(ring[d], xr, v);
-        reduce_store<NMAT, B>(v, p, part, a.slices, lane);
-      }
+      idx[(d + D - 1) % D] = nxt;
     }
   }
   __syncthreads();
