@@ -266,9 +266,11 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
 
   // Batches are handed out in order from a workgroup counter in LDS, so a wave that runs ahead
   // (the three waves of a SIMD progress unevenly) takes more of them and all waves finish
-  // together. The first D - 1 batches of each wave are dealt round-robin (index wave +
-  // kWaves d) and loaded while x is staged; an index past the last batch loads the last one
-  // (no branch, so that the wait counts stay exact) and is never computed.
+  // together. The first D batches of each wave are dealt round-robin (index wave + kWaves d):
+  // D - 1 loaded while x is staged (an index past the last batch loads the last one, with no
+  // branch, so that the wait counts stay exact, and is never computed), the D-th the wave's
+  // first ticket. Each ticket after that is taken from the counter one batch ahead, so that
+  // its round trip overlaps the batch being summed.
   __shared__ int next_batch;
   BatchT ring[D];
   int idx[D];
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
     idx[d] = wave + kWaves * d;
     load_batch<FMT, NMAT, J, B>(ring[d], a, row0, batch_pos(min(idx[d], nb - 1), nbs, nr, B), lane);
   }
-  if (threadIdx.x == 0) next_batch = kWaves * (D - 1);
+  if (threadIdx.x == 0) next_batch = kWaves * D;
   {
     const int n16 = a.k * (XB ? 2 : 4) / 16;
     const uint4* src = static_cast<const uint4*>(a.x);
@@ -294,21 +296,17 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
       cur = p.s;
     }
   };
-  auto take = [&]() -> int {                          // the next batch index, the same in every lane
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&next_batch, 1);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
-  // Steady state: slot d holds a loaded batch; the next index is taken and, while it is a
-  // batch, its loads go into the free slot as slot d is computed (no load is conditional on
-  // this path). Indices only grow, so once one is past the end the wave computes the D - 1
-  // slots still in flight that hold a batch, in order, and stops.
+  int ticket = wave + kWaves * (D - 1);               // the batch after the ring's, same in every lane
+  // Steady state: slot d holds a loaded batch; while the ticket is a batch, its loads go into
+  // the free slot as slot d is computed (no load is conditional on this path) and the next
+  // ticket is fetched. Indices only grow, so once one is past the end the wave computes the
+  // D - 1 slots still in flight that hold a batch, in order, and stops.
   bool live = true;
   while (live) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (!live) break;
-      const int nxt = take();
+      const int nxt = ticket;
       if (nxt >= nb) {
 #pragma unroll
         for (int e = 0; e < D - 1; ++e) {
@@ -325,6 +323,8 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
         break;
       }
       // here idx[d] < nb too: every index dealt before nxt is smaller than it
+      int pending = 0;                                // read back only after this batch is summed
+      if (lane == 0) pending = atomicAdd(&next_batch, 1);
       const BatchPos p = batch_pos(idx[d], nbs, nr, B);
       x_for(p);
       float v[B * NMAT];
@@ -332,6 +332,7 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
                                         v, lane);
       reduce_store<NMAT, B>(v, p, part, a.slices, lane);
       idx[(d + D - 1) % D] = nxt;
+      ticket = __builtin_amdgcn_readfirstlane(pending);
     }
   }
   __syncthreads();
