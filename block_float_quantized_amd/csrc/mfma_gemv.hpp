@@ -494,12 +494,32 @@ template <int FMT, int NMAT> constexpr int kG = FMT == 4 ? 2 : 1;
 
 // K slices and steps per slice, from N and K alone: about 1024 workgroups in all, at most 16
 // slices, at least one step per slice.
+// Slices of K: the count that minimises (rounds of resident workgroups) x (fixed start of a
+// workgroup + its steps), plus the slice partials' cost (an eighth of a step per slice, and a
+// step for the slice-sum launch itself). Two workgroups stay resident on each compute unit,
+// 512 on the 256 of an MI355X (a constant, not the device's count: the slicing, hence every
+// summation order, must depend on N and K alone); a workgroup's first operands take about two
+// steps' time to arrive. A grid slightly larger than the resident slots costs a whole second
+// round for its last few workgroups. Matrices with two rounds of column groups are not sliced.
+constexpr int kResidentSlots = 512;
+constexpr int kStartSteps = 2;
 inline void pick_slices(int n, int k, int sk_values, int& ks, int& sps) {
   const int groups = (n + kCols - 1) / kCols;
   const int nst = (k + sk_values - 1) / sk_values;
-  int want = 1;
-  while (want < 16 && groups * want < 1024 && want * 2 <= nst) want *= 2;
-  sps = (nst + want - 1) / want;
+  ks = 1;
+  sps = nst;
+  if (groups >= 2 * kResidentSlots) return;
+  long best = -1;
+  for (int p = nst; p >= 1; --p) {                 // steps per slice, fewest slices first
+    const int s = (nst + p - 1) / p;
+    if (s > 64) break;
+    const long rounds = ((long)groups * s + kResidentSlots - 1) / kResidentSlots;
+    const long cost = 8 * rounds * (kStartSteps + p) + s + (s > 1 ? 8 : 0);   // in eighths of a step
+    if (best < 0 || cost < best) {
+      best = cost;
+      sps = p;
+    }
+  }
   ks = (nst + sps - 1) / sps;
 }
 
