@@ -528,7 +528,7 @@ __device__ __forceinline__ void exact_logits(const uint16_t* x, const uint16_t* 
 __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
   const RouteArgs& a = c.r;
   __shared__ int cand[4][256];
-  __shared__ double cval[4][256];
+  __shared__ double cval[4][257];            // candidate logits, then the shared-expert logit
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= a.m) return;
@@ -588,23 +588,21 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
       hi[q] = -__builtin_huge_val();
     }
   }
-  // k-th largest lower end
-  double lk = __builtin_huge_val();
+  // k-th largest lower end: the lower ends staged in this wave's row of cval (expert e at
+  // position e), then the wave's top-k selection over them; the last value it takes
+  double lk;
   {
-    // per round: the largest remaining lower end (exact max-reduction), removed once from the
-    // lowest lane holding it (its first slot holding it); no divergent branch
-    double v[4] = {lo[0], lo[1], lo[2], lo[3]};
-    for (int j = 0; j < a.top_k; ++j) {
-      const double bv = fmax(fmax(v[0], v[1]), fmax(v[2], v[3]));
-      const double mv = wave_max_f64(bv);
-      lk = mv;
-      const uint64_t b = __ballot(bv == mv);
-      const int ml = b ? __builtin_ctzll(b) : -1;
-      bool done = lane != ml;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (!done && v[q] == mv) { v[q] = -__builtin_huge_val(); done = true; }
-    }
+    for (int q = 0; q < 4; ++q) cval[wv][lane + 64 * q] = lo[q];
+    __builtin_amdgcn_wave_barrier();
+    double sl[8];
+    int sp[8];
+    tk::topk_select(cval[wv], a.n_exp, a.top_k, lane, sl, sp);
+    lk = sl[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+      if (j == a.top_k - 1) lk = sl[j];
+    __builtin_amdgcn_wave_barrier();
   }
   // candidates, in expert order
   int nc = 0;
@@ -640,52 +638,18 @@ __global__ __launch_bounds__(256) void certify_topk_kernel(CertArgs c) {
     const uint16_t* rows[1] = {a.sh_gate_w};
     exact_logits<1>(xr, rows, a.hidden, lane, &glog);
   }
+  // top-k among the candidates by (exact logit desc, expert asc): candidates are in expert
+  // order, so the selection over their positions (a NaN ranks below every number) picks them
+  // in that order; the shared-expert logit goes after them for the gate
+  if (lane == 0) cval[wv][nc] = glog;
   __builtin_amdgcn_wave_barrier();
-  // top-k among the candidates by (exact logit desc, expert asc)
-  double v[4];
-  int ix[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int i = lane + 64 * q;
-    ix[q] = i < nc ? cand[wv][i] : 0x7fffffff;
-    const double cv = i < nc ? cval[wv][i] : -__builtin_huge_val();
-    v[q] = cv != cv ? -__builtin_huge_val() : cv;         // a NaN logit ranks below every number
-  }
   double sel_l[8];
-  int sel_e[8];
-  for (int j = 0; j < a.top_k; ++j) {
-    // the largest remaining exact logit, then the first candidate holding it: candidates are
-    // in expert order, candidate 64 q + lane, so the first q with a match and its lowest lane
-    const double M = wave_max_f64(fmax(fmax(v[0], v[1]), fmax(v[2], v[3])));
-    int bq = -1, bl = 0;
+  int sel_p[8], sel_e[8];
+  tk::topk_select(cval[wv], nc, a.top_k, lane, sel_l, sel_p);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint64_t b = __ballot(ix[q] != 0x7fffffff && v[q] == M);
-      if (bq < 0 && b != 0) { bq = q; bl = __builtin_ctzll(b); }
-    }
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q == bq) bi = __builtin_amdgcn_readlane(ix[q], bl);
-    sel_l[j] = M;
-    sel_e[j] = bi;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q == bq && lane == bl) { v[q] = -__builtin_huge_val(); ix[q] = 0x7fffffff; }
-  }
-  double ex = 0.0, lj = sel_l[0];
-  int ej = sel_e[0];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j == lane && j < a.top_k) { lj = sel_l[j]; ej = sel_e[j]; }
-  if (lane < a.top_k) ex = exp(lj - sel_l[0]);
-  double z = 0.0;
-  for (int j = 0; j < a.top_k; ++j) z += __shfl(ex, j);
-  if (lane < a.top_k) {
-    a.ids[(int64_t)t * a.top_k + lane] = ej;
-    a.w[(int64_t)t * a.top_k + lane] = (float)(ex / z);
-  }
-  if (a.g && lane == 0) a.g[t] = a.sh_gate_w ? (float)(1.0 / (1.0 + exp(-glog))) : 1.0f;
+  for (int j = 0; j < 8; ++j) sel_e[j] = j < a.top_k ? cand[wv][sel_p[j]] : 0;
+  tk::topk_store(cval[wv], nc, a.top_k, a.sh_gate_w != nullptr, lane, sel_l, sel_e, a.ids + (int64_t)t * a.top_k,
+                 a.w + (int64_t)t * a.top_k, a.g ? a.g + t : nullptr, nullptr);
 }
 
 }  // namespace
