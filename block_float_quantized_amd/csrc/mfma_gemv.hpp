@@ -467,7 +467,9 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_gemv_kernel(MgArgs a) {
       }
 }
 
-// y[i][j] = epilogue(sum over slices s = 0, 1, ... of the partials), in slice order.
+// y[i][j] = epilogue(sum over slices s = 0, 1, ... of the partials), in slice order. The loads
+// of eight slices (of every matrix) are issued before their additions, so that a call costs one
+// memory round trip per eight slices instead of one per slice.
 template <int NMAT>
 __global__ __launch_bounds__(256) void slice_sum_kernel(MgArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -475,10 +477,18 @@ __global__ __launch_bounds__(256) void slice_sum_kernel(MgArgs a) {
   if (idx >= mn) return;
   float v[NMAT];
 #pragma unroll
-  for (int t = 0; t < NMAT; ++t) {
-    float sum = 0.f;
-    for (int sl = 0; sl < a.ks; ++sl) sum += a.ws[((int64_t)sl * NMAT + t) * mn + idx];
-    v[t] = sum;
+  for (int t = 0; t < NMAT; ++t) v[t] = 0.f;
+  for (int s0 = 0; s0 < a.ks; s0 += 8) {
+    float p[NMAT][8];
+#pragma unroll
+    for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) p[t][u] = a.ws[((int64_t)min(s0 + u, a.ks - 1) * NMAT + t) * mn + idx];
+#pragma unroll
+    for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < a.ks) v[t] += p[t][u];
   }
   float out = v[0];
   if constexpr (NMAT == 2) out = out / (1.0f + __expf(-out)) * v[1];
@@ -492,8 +502,6 @@ __global__ __launch_bounds__(256) void slice_sum_kernel(MgArgs a) {
 // 128-value units per step, from the format alone.
 template <int FMT, int NMAT> constexpr int kG = FMT == 4 ? 2 : 1;
 
-// K slices and steps per slice, from N and K alone: about 1024 workgroups in all, at most 16
-// slices, at least one step per slice.
 // Slices of K: the count that minimises (rounds of resident workgroups) x (fixed start of a
 // workgroup + its steps), plus the slice partials' cost (an eighth of a step per slice, and a
 // step for the slice-sum launch itself). Two workgroups stay resident on each compute unit,
