@@ -145,27 +145,44 @@ hipError_t launch_x(const MoeGemvArgs& ma, hipStream_t s) {
 }
 
 // y[t][n] = sum_j w[t][j] * o[inv[t*K+j]][n] + g[t] * o[m*K + t][n]; four outputs per thread.
+// The weights and positions of all slots (top_k <= 8) are loaded first, then all their rows,
+// with the shared expert's, then the products are added in rank order: two memory round trips
+// per token, not two per slot.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.y;
   const int n4 = blockIdx.x * 256 + threadIdx.x;
   if (n4 * 4 >= a.hidden) return;
+  float wj[8];
+  int pos[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int jj = min(j, a.top_k - 1);
+    wj[j] = a.w[(int64_t)t * a.top_k + jj];
+    pos[j] = a.inv[(int64_t)t * a.top_k + jj];
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = *reinterpret_cast<const f32x4*>(a.o + (int64_t)pos[j] * a.hidden + n4 * 4);
+  float gt = 0.f;                                     // the shared expert's gate and row
+  f32x4 os = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.g) {
+    gt = a.g[t];
+    os = *reinterpret_cast<const f32x4*>(a.o + ((int64_t)a.m * a.top_k + t) * a.hidden + n4 * 4);
+  }
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.top_k; ++j) {
-    const float wj = a.w[(int64_t)t * a.top_k + j];
-    const int pos = a.inv[(int64_t)t * a.top_k + j];
-    const f32x4 o = *reinterpret_cast<const f32x4*>(a.o + (int64_t)pos * a.hidden + n4 * 4);
-    acc.x = __builtin_fmaf(wj, o.x, acc.x);
-    acc.y = __builtin_fmaf(wj, o.y, acc.y);
-    acc.z = __builtin_fmaf(wj, o.z, acc.z);
-    acc.w = __builtin_fmaf(wj, o.w, acc.w);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= a.top_k) break;
+    acc.x = __builtin_fmaf(wj[j], o[j].x, acc.x);
+    acc.y = __builtin_fmaf(wj[j], o[j].y, acc.y);
+    acc.z = __builtin_fmaf(wj[j], o[j].z, acc.z);
+    acc.w = __builtin_fmaf(wj[j], o[j].w, acc.w);
   }
   if (a.g) {
-    const float gt = a.g[t];
-    const f32x4 o = *reinterpret_cast<const f32x4*>(a.o + ((int64_t)a.m * a.top_k + t) * a.hidden + n4 * 4);
-    acc.x = __builtin_fmaf(gt, o.x, acc.x);
-    acc.y = __builtin_fmaf(gt, o.y, acc.y);
-    acc.z = __builtin_fmaf(gt, o.z, acc.z);
-    acc.w = __builtin_fmaf(gt, o.w, acc.w);
+    acc.x = __builtin_fmaf(gt, os.x, acc.x);
+    acc.y = __builtin_fmaf(gt, os.y, acc.y);
+    acc.z = __builtin_fmaf(gt, os.z, acc.z);
+    acc.w = __builtin_fmaf(gt, os.w, acc.w);
   }
   *reinterpret_cast<f32x4*>(a.y + (int64_t)t * a.hidden + n4 * 4) = acc;
 }
