@@ -20,7 +20,8 @@
 //    touches 16 lines and uses 64 bytes of each), the block exponents into registers. Each
 //    ring slot is a separate LDS array named at compile time (the loop is unrolled over a
 //    4-step cycle), so the compiler can tell the slot being read from those being filled;
-//    one barrier per step, after a counted wait for the step's own loads.
+//    one barrier per step, after a counted wait for the step's own loads and for the
+//    wave's LDS reads of the slots refilled next.
 //  * v_mfma_f32_32x32x16_bf16 with fp32 accumulation; each wave owns all 128 rows of the
 //    tile and 64 output columns.
 //    A and B share one permutation of K inside every 8-value group (the order the BFP4
@@ -174,11 +175,16 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
   return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
 }
 
-// s_waitcnt vmcnt(n), every other counter left alone
+// s_waitcnt vmcnt(n) lgkmcnt(0), expcnt left alone. Before the step's barrier a wave needs
+// both: its own loads of the step landed, and its LDS reads of the previous step returned.
+// The slot those reads used is refilled right after the barrier, and a read still queued in
+// the LDS unit can be overtaken by another wave's load-to-LDS write arriving on the memory
+// return path (the compiler waits for a read only where its MFMA consumes it, often after
+// the barrier).
 template <int N>
-__device__ __forceinline__ void wait_vm() {
+__device__ __forceinline__ void wait_vm_lds() {
   static_assert(N >= 0 && N <= 63, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xF) | (N & 0xF) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 0xF) | ((N >> 4) << 14));
 }
 
 // keeps the compiler from moving memory accesses across this point
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
     constexpr int I = decltype(IC)::value;
     constexpr int SP = I % 4;
     constexpr int NRT = decltype(NC)::value;
-    wait_vm<SP == 0 ? 0 : SP == 1 ? 6 : SP == 2 ? 0 : 4>();
+    wait_vm_lds<SP == 0 ? 0 : SP == 1 ? 6 : SP == 2 ? 0 : 4>();
     mem_order();
     __builtin_amdgcn_s_barrier();
     mem_order();

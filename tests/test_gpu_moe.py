@@ -196,6 +196,30 @@ def test_moe_prefill_chunk_2048(moe_full):
     _prefill_check(layer, devb, bank, x, bias, np.arange(2048))
 
 
+def test_moe_prefill_repeatable(moe_full):
+    """The 2,048-token chunk run 24 times, each over a workspace filled with other random
+    bytes: every output bit for bit the same. Guards the LDS ring of the grouped GEMMs (a
+    slot refilled while another wave's reads of it were still queued once changed a few
+    outputs of one wave's columns in rare runs) and any read of workspace not written."""
+    layer, dev, bank = moe_full
+    note("moe prefill m=2048 repeatability")
+    devb = bfq.MoeLayer(**{**dev.__dict__, "router_bias": dev_f32(synth.router_bias(0))})
+    m = 2048
+    x = dev_bf16(synth.moe_tokens(m, 0, cfg_id=5))
+    ws = torch.empty((bfq.bfp_moe_workspace_bytes(devb, m),), dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda")
+    first = None
+    for r in range(24):
+        gen.manual_seed(1000 + r)
+        ws.random_(0, 256, generator=gen)
+        y = bfq.bfp_moe_forward(devb, x, workspace=ws)
+        if first is None:
+            first = y.clone()
+        else:
+            bad = (y != first).any(1).nonzero().flatten().tolist()
+            assert not bad, f"run {r}: tokens {bad[:8]} differ from the first run"
+
+
 def test_moe_prefill_and_decode_agree(moe_full):
     """The same 33 tokens through the prefill path and through 33 single-token decodes:
     identical routing, outputs equal up to the bf16 rounding of h in prefill."""
