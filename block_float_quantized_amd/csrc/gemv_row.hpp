@@ -100,11 +100,12 @@ __device__ __forceinline__ void load_batch(Batch<FMT, NMAT, J, B>& g, const RowA
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     const int64_t row = row0 + p.r0 + min(b, p.count - 1);      // clamped: no branch
+    const int64_t blk0 = (int64_t)p.s * J * kWave;
 #pragma unroll
     for (int t = 0; t < NMAT; ++t)
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int64_t blk = (int64_t)p.s * J * kWave + j * kWave + lane;
+        const int64_t blk = blk0 + j * kWave + lane;
         g.c[b][t][j] = __builtin_nontemporal_load(reinterpret_cast<const T*>(a.code[t] + row * cpr) + blk);
         g.e[b][t][j] = __builtin_nontemporal_load(a.exp[t] + row * nbk + blk);
       }
@@ -202,16 +203,18 @@ __device__ __forceinline__ void load_and_sum(Batch<FMT, NMAT, J, B>& ld, const R
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     const int64_t row = row0 + pl.r0 + min(b, pl.count - 1);
+    const int64_t blk0 = (int64_t)pl.s * J * kWave;
 #pragma unroll
     for (int t = 0; t < NMAT; ++t) {
-      float acc = 0.f;
+      float acc;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int64_t blk = (int64_t)pl.s * J * kWave + j * kWave + lane;
+        const int64_t blk = blk0 + j * kWave + lane;
         ld.c[b][t][j] = __builtin_nontemporal_load(reinterpret_cast<const T*>(a.code[t] + row * cpr) + blk);
         ld.e[b][t][j] = __builtin_nontemporal_load(a.exp[t] + row * nbk + blk);
         __builtin_amdgcn_sched_barrier(0);
-        acc += unit_sum<FMT, NMAT, XB, J, B>(g, xr, b, t, j);
+        const float u = unit_sum<FMT, NMAT, XB, J, B>(g, xr, b, t, j);
+        acc = j == 0 ? u : acc + u;
         __builtin_amdgcn_sched_barrier(0);
       }
       v[b * NMAT + t] = acc;
@@ -227,9 +230,12 @@ __device__ __forceinline__ void sum_batch(const Batch<FMT, NMAT, J, B>& g, const
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int t = 0; t < NMAT; ++t) {
-      float acc = 0.f;
+      float acc;
 #pragma unroll
-      for (int j = 0; j < J; ++j) acc += unit_sum<FMT, NMAT, XB, J, B>(g, xr, b, t, j);
+      for (int j = 0; j < J; ++j) {
+        const float u = unit_sum<FMT, NMAT, XB, J, B>(g, xr, b, t, j);
+        acc = j == 0 ? u : acc + u;
+      }
       v[b * NMAT + t] = acc;
     }
 }
@@ -258,7 +264,9 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
   float* part = reinterpret_cast<float*>(smem + xbytes);
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  // wave-uniform (readfirstlane): batch indices, rows and load bases then live in scalar
+  // registers, and the vector unit only does the per-lane work
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int row0 = blockIdx.x * a.rows;
   const int nr = min(a.rows, a.n - row0);
   const int nbs = (nr + B - 1) / B;                  // batches per slice

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_gemv_kernel(MgArgs a) {
   constexpr int SK = 128 * G, LV = SK / 4;
   extern __shared__ __align__(16) uint16_t lds[];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar row arithmetic
   const int c = lane & 15, g = lane >> 4;
   const int col0 = blockIdx.x * kCols + wave * 16;
 

@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kWave * 9) void tok_down_kernel(MoeTokArgs ma) {
   __shared__ float os[9][RPW];
   const int ns = blockDim.x / kWave;               // slots: top_k (+ 1 shared)
   const int t = blockIdx.y;
-  const int d = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int d = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;   // d wave-uniform
   const bool shared = d == ma.top_k;
   const int32_t* ids = ma.ids + (int64_t)t * ma.top_k;
   const float* wt = ma.w + (int64_t)t * ma.top_k;

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kPT, 2) void grouped_gemm_kernel(PfArgs a) {
   if (!find_tile<TN>(a, t)) return;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave wave-uniform
   const int g = lane / 32, lc = lane % 32;
   // A row (token row of x, or pair row of h) of tile row rr; rows past the group read the
   // group's first row: their results are never stored
