@@ -332,7 +332,8 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
       }
       // here idx[d] < nb too: every index dealt before nxt is smaller than it
       int pending = 0;                                // read back only after this batch is summed
-      if (lane == 0) pending = atomicAdd(&next_batch, 1);
+      if (lane == 0)                                  // increment (not add): kept as one LDS op whose result is read late
+        pending = (int)__builtin_amdgcn_atomic_inc32(reinterpret_cast<uint32_t*>(&next_batch), 0x7fffffffu, __ATOMIC_RELAXED, "workgroup");
       const BatchPos p = batch_pos(idx[d], nbs, nr, B);
       x_for(p);
       float v[B * NMAT];
