@@ -372,10 +372,15 @@ def timed_graph(fn, outs, calls: int = 64, reps: int = 10):
         return None
 
 
+GRAPH_LEAD_SPIN = 200_000   # device clock cycles (torch.cuda._sleep) ahead of a timed graph replay
+
+
 def graph_steps(fn, outs, steps: int, warmup: int):
     """ms per step over exactly `steps` consecutive steps fn(0), ..., fn(steps - 1) launched as one
     HIP graph replay, after `warmup` steps fn(0), ..., fn(warmup - 1) launched as the replay of a
-    second graph (untimed). First, three replays of the timed graph (each after eager work that
+    second graph (untimed), a synchronisation and a short device spin (so that the start event
+    is taken when the device reaches the graph, not while the host still submits it). First,
+    three replays of the timed graph (each after eager work that
     zeroes the outputs, and a synchronisation) must leave every tensor in `outs` bit-identical
     to an eager run of the same steps; else (or if capture fails) None. Returns ms per step."""
     import torch
@@ -416,6 +421,10 @@ def graph_steps(fn, outs, steps: int, warmup: int):
         stream = torch.cuda.current_stream()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
+        # a device spin ahead of the start event keeps the idle GPU from taking the event at
+        # once: the host then finishes submitting the graph's packets while the spin runs,
+        # so the timed span holds the K steps and not the host's graph submission
+        torch.cuda._sleep(GRAPH_LEAD_SPIN)
         t0.record(stream)
         gk.replay()
         t1.record(stream)

@@ -16,7 +16,9 @@
 //    codes, 64 B of exponents).
 //  * One workgroup of twelve waves per compute unit (its LDS request keeps a second one off the
 //    unit), each owning an equal share of the rows: every unit streams the same weight bytes.
-//    The workgroup stages x in LDS once; a wave keeps its lanes' x values of the current slice
+//    The workgroup stages x in LDS once, by load-to-LDS buffer loads issued before the first
+//    weight loads (a register copy issued after them had to wait for them: loads complete
+//    in order); a wave keeps its lanes' x values of the current slice
 //    in registers (bf16 pairs in the unpack's pair order, or fp32), so no weight is ever
 //    matched against x read back from LDS.
 //  * A workgroup's tasks are cut into batches of B rows of one slice (slice by slice), handed to
@@ -280,6 +282,19 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
   // first ticket. Each ticket after that is taken from the counter one batch ahead, so that
   // its round trip overlaps the batch being summed.
   __shared__ int next_batch;
+  // The activation row goes straight into LDS (load-to-LDS buffer loads: no registers),
+  // issued before the weight ring, so that the wave's wait for it does not include the
+  // weights: each instruction moves 64 chunks of 16 bytes, and the row is a whole number of
+  // such groups (K is a multiple of 1024).
+  {
+    const int n16 = a.k * (XB ? 2 : 4) / 16;
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0, n16 * 16,
+                                                                         0x00020000);
+    for (int c0 = wave * kWave; c0 < n16; c0 += kThreads)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void*)(smem + c0 * 16), 16,
+                                               (uint32_t)(c0 + lane) * 16u, 0, 0, 0);
+  }
+  asm volatile("" ::: "memory");
   BatchT ring[D];
   int idx[D];
 #pragma unroll
@@ -287,12 +302,13 @@ __global__ __launch_bounds__(kThreads) void row_gemv_kernel(RowArgs a) {
     idx[d] = wave + kWaves * d;
     load_batch<FMT, NMAT, J, B>(ring[d], a, row0, batch_pos(min(idx[d], nb - 1), nbs, nr, B), lane);
   }
+  asm volatile("" ::: "memory");
   if (threadIdx.x == 0) next_batch = kWaves * D;
+  // vmcnt(ring loads): every load issued before the ring (the wave's x chunks) has landed
   {
-    const int n16 = a.k * (XB ? 2 : 4) / 16;
-    const uint4* src = static_cast<const uint4*>(a.x);
-    uint4* dst = static_cast<uint4*>(xs);
-    for (int i = threadIdx.x; i < n16; i += kThreads) dst[i] = src[i];
+    constexpr int kRingLoads = (D - 1) * B * NMAT * J * 2;
+    static_assert(kRingLoads <= 63, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xF) | (kRingLoads & 0xF) | ((kRingLoads >> 4) << 14));
   }
   __syncthreads();
 
