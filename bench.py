@@ -232,6 +232,12 @@ def log(msg):
 BUSY = {"on": False}
 BUSY_CALLS = 20
 MARKER_KERNEL = "spin_kernel"      # torch.cuda._sleep
+MARKER_MAX_NS = 20_000             # a marker spin (1000 cycles) lasts a few us; the spin ahead of
+                                   # a timed graph replay (GRAPH_LEAD_SPIN) ~85 us, not a marker
+
+
+def is_marker(name: str, duration_ns) -> bool:
+    return MARKER_KERNEL in name and duration_ns < MARKER_MAX_NS
 
 
 def busy_segment(name: str, fn):
@@ -259,7 +265,7 @@ def segment_summary(trace_dir: str, stderr_file: str):
     db = glob.glob(os.path.join(trace_dir, "**", "*.db"), recursive=True)[0]
     rows = sorted(sqlite3.connect(db).execute("select name, start, end from kernels").fetchall(),
                   key=lambda r: r[1])
-    marks = [i for i, r in enumerate(rows) if MARKER_KERNEL in r[0]]
+    marks = [i for i, r in enumerate(rows) if is_marker(r[0], r[2] - r[1])]
     print(f"| workload | calls | device busy per call (us) | span per call (us) | kernels per call | largest kernel (share) |")
     print("|---|---:|---:|---:|---:|---|")
     for j, name in enumerate(names):
@@ -745,7 +751,7 @@ def counter_report(dirs):
             "order by dispatch_id").fetchall()
         seg, inside, last = -1, False, None
         for did, kname, cn, v, du in rows:
-            if MARKER_KERNEL in kname:
+            if is_marker(kname, du):
                 if did != last:
                     inside = not inside
                     if inside:
