@@ -533,7 +533,7 @@ def run_mlp(args, m, mats, xb, batch_invariant=False, graph=False):
 
 def cpu_threads() -> int:
     """Host threads the oracle may use: the cores this process may run on, capped by
-    OMP_NUM_THREADS when that is set (a GPU machine grants a share of its host)."""
+    OMP_NUM_THREADS when that is set (a shared host may grant only part of its cores)."""
     n = len(os.sched_getaffinity(0))
     env = os.environ.get("OMP_NUM_THREADS", "")
     return min(n, int(env)) if env.isdigit() and int(env) > 0 else n
