@@ -695,6 +695,15 @@ def counter_driver():
     y = torch.empty((1, HIDDEN), dtype=torch.bfloat16, device="cuda")
     segment("dense BFP4 MLP M=1", lambda i: (bfq.bfp_gemm(mats[i % 8][0], x, w_up=mats[i % 8][1], out=h),
                                              bfq.bfp_gemm(mats[i % 8][2], h, out_dtype=torch.bfloat16, out=y)))
+    for m in (8, 16):
+        xm = bf16_dev(synth.mlp_case(m, 0)["x"])
+        hm = torch.empty((m, INTER), dtype=torch.float32, device="cuda")
+        ymm = torch.empty((m, HIDDEN), dtype=torch.bfloat16, device="cuda")
+        g0, u0, d0 = mats[0]
+        wsg = workspace(max(bfq.bfp_gemm_workspace_bytes(g0, m, u0), bfq.bfp_gemm_workspace_bytes(d0, m)))
+        segment(f"dense BFP4 MLP M={m}",
+                lambda i: (bfq.bfp_gemm(mats[i % 8][0], xm, w_up=mats[i % 8][1], out=hm, workspace=wsg),
+                           bfq.bfp_gemm(mats[i % 8][2], hm, out_dtype=torch.bfloat16, out=ymm, workspace=wsg)))
     del mats, c
     torch.cuda.empty_cache()
     g = synth.gemv_case(0)
@@ -736,11 +745,14 @@ def counter_report(dirs):
     """Per workload (segments between marker kernels, in the driver's order) and kernel: the
     mean per dispatch of each counter collected; bytes calibrated by the copy (FETCH_SIZE and
     WRITE_SIZE in KiB), L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS), VALU issue = 4 cycles per
-    wave64 VALU instruction per SIMD (1024) over the GPU cycles (GRBM_GUI_ACTIVE / 8 XCDs)."""
+    wave64 VALU instruction per SIMD (1024) over the GPU cycles (GRBM_GUI_ACTIVE / 8 XCDs);
+    matrix busy = SQ_VALU_MFMA_BUSY_CYCLES per SIMD over the GPU cycles, LDS active and
+    bank-conflict = SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT per CU (256) over the GPU cycles,
+    waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES, TA stalled = TA_ADDR_STALLED_BY_TC_CYCLES per CU."""
     import glob
     import sqlite3
-    names = ["dense BFP4 MLP M=1", "BFP8 GEMV 2048x2048 M=1", "BFP8 QKV 2048->5120 M=1", "BFP8 O 4096->2048 M=1",
-             "BFP8 LM head 2048->151936 M=1", "moe decode M=1"]
+    names = ["dense BFP4 MLP M=1", "dense BFP4 MLP M=8", "dense BFP4 MLP M=16", "BFP8 GEMV 2048x2048 M=1",
+             "BFP8 QKV 2048->5120 M=1", "BFP8 O 4096->2048 M=1", "BFP8 LM head 2048->151936 M=1", "moe decode M=1"]
     vals = {}        # (segment, kernel) -> counter -> [values]
     dur = {}
     copy = {}
@@ -771,8 +783,9 @@ def counter_report(dirs):
     kib = COPY_BYTES / 1024
     ff = kib / mean(copy["FETCH_SIZE"]) if "FETCH_SIZE" in copy else None
     fw = kib / mean(copy["WRITE_SIZE"]) if "WRITE_SIZE" in copy else None
-    print("| workload | kernel | dispatches | avg (us) | HBM read MB | HBM written MB | L2 hit | VALU issue |")
-    print("|---|---|---:|---:|---:|---:|---:|---:|")
+    print("| workload | kernel | dispatches | avg (us) | HBM read MB | HBM written MB | L2 hit | VALU issue "
+          "| matrix busy | LDS active | LDS bank-conflict | waiting | TA stalled by TC (cycles per CU) |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
     for (wl, k), cs in vals.items():
         n = len(dur[(wl, k)])
         us = mean(list(dur[(wl, k)].values())) / 1000.0
@@ -782,11 +795,15 @@ def counter_report(dirs):
         if "TCC_HIT_sum" in cs and "TCC_MISS_sum" in cs:
             h_, m_ = mean(cs["TCC_HIT_sum"]), mean(cs["TCC_MISS_sum"])
             hit = f"{100 * h_ / max(h_ + m_, 1):.0f}%"
-        valu = ""
-        if "SQ_INSTS_VALU" in cs and "GRBM_GUI_ACTIVE" in cs:
-            cyc = mean(cs["GRBM_GUI_ACTIVE"]) / 8
-            valu = f"{100 * mean(cs['SQ_INSTS_VALU']) * 4 / 1024 / max(cyc, 1):.0f}%"
-        print(f"| {wl} | `{k}` | {n} | {us:.2f} | {rd} | {wr} | {hit} | {valu} |")
+        cyc = mean(cs["GRBM_GUI_ACTIVE"]) / 8 if "GRBM_GUI_ACTIVE" in cs else None
+        pct = lambda c_, units: f"{100 * mean(cs[c_]) / units / max(cyc, 1):.0f}%" if c_ in cs and cyc else ""
+        valu = f"{100 * mean(cs['SQ_INSTS_VALU']) * 4 / 1024 / max(cyc, 1):.0f}%" if "SQ_INSTS_VALU" in cs and cyc else ""
+        mfma, lds, ldc = pct("SQ_VALU_MFMA_BUSY_CYCLES", 1024), pct("SQ_LDS_IDX_ACTIVE", 256), pct("SQ_LDS_BANK_CONFLICT", 256)
+        wait = ""
+        if "SQ_WAIT_ANY" in cs and "SQ_WAVE_CYCLES" in cs:
+            wait = f"{100 * mean(cs['SQ_WAIT_ANY']) / max(mean(cs['SQ_WAVE_CYCLES']), 1):.0f}%"
+        ta = f"{mean(cs['TA_ADDR_STALLED_BY_TC_CYCLES']) / 256:,.0f}" if "TA_ADDR_STALLED_BY_TC_CYCLES" in cs else ""
+        print(f"| {wl} | `{k}` | {n} | {us:.2f} | {rd} | {wr} | {hit} | {valu} | {mfma} | {lds} | {ldc} | {wait} | {ta} |")
     if ff and fw:
         print(f"\ncalibration: the copy reads and writes {kib:.0f} KiB per dispatch; FETCH_SIZE factor {ff:.4f}, "
               f"WRITE_SIZE factor {fw:.4f}")
