@@ -59,8 +59,8 @@ struct MgArgs {
   int sps;           // steps per slice
   int kc;            // K values staged per chunk (a whole number of steps)
   int exp_vec;       // a lane's exponent bytes may be read with one aligned load
-  int exp_grp;       // every step whole and the exponent arrays aligned to a step's exponent
-                     // bytes: exponents are loaded four steps at a time (load_exp4)
+  int whole;         // every step whole, BFP4 rows 16-byte aligned and exp_vec: the loads of a
+                     // step take one form, with no branches (see the kernel's steady loop)
   int code16;        // BFP4 rows start on 16-byte boundaries (K a multiple of 32)
   uint64_t* cand;    // argmax mode: workspace (argmax_workspace_bytes), else null
   int32_t* am_idx;   // argmax mode: per activation row, the column of the largest output
@@ -171,7 +171,7 @@ __device__ __forceinline__ void stage(uint16_t* xs, const MgArgs& a, int kb, int
 // Load step st (K values [st SK, (st + 1) SK)) of one matrix, rows row0 .. row0 + 15 (clamped
 // to n - 1), in the row-contiguous lane order of StepRegs. K is a multiple of 16: in the last
 // step a row holds a whole number of 16-value blocks, zeros after.
-template <int FMT, int G, bool EXP = true>
+template <int FMT, int G, bool WHOLE = false>
 __device__ __forceinline__ void load_step(StepRegs<FMT, G>& r, const uint8_t* code, const uint8_t* exp,
                                           int row0, const MgArgs& a, int st, int lane) {
   using R = StepRegs<FMT, G>;
@@ -182,7 +182,7 @@ __device__ __forceinline__ void load_step(StepRegs<FMT, G>& r, const uint8_t* co
   const int nbk = a.k / kBlock;
   const int64_t row_bytes = FMT == 8 ? (int64_t)a.k : (int64_t)a.k / 2;
   const int kb0 = st * SK;                          // first K value of the step
-  const bool full = kb0 + SK <= a.k;
+  const bool full = WHOLE || kb0 + SK <= a.k;
   // codes
 #pragma unroll
   for (int q = 0; q < R::kLoads; ++q) {
@@ -192,7 +192,7 @@ __device__ __forceinline__ void load_step(StepRegs<FMT, G>& r, const uint8_t* co
     const uint8_t* cp = code + row * row_bytes + (FMT == 8 ? kb0 : kb0 / 2) + cb;
     const int v0 = kb0 + (FMT == 8 ? cb : 2 * cb);  // first K value of these 16 bytes
     if (full) {
-      if (FMT == 8 || a.code16) {
+      if (FMT == 8 || WHOLE || a.code16) {
         r.c[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp));
       } else {
         // BFP4 rows of K/2 bytes with K an odd multiple of 16 are only 8-byte aligned
@@ -214,11 +214,11 @@ __device__ __forceinline__ void load_step(StepRegs<FMT, G>& r, const uint8_t* co
     }
   }
   // exponents: lane i takes bytes [(i % 4) EPL, +EPL) of row i / 4
-  if constexpr (EXP) {
+  {
     const int64_t row = min(row0 + lane / 4, a.n - 1);
     const int b0 = (lane % 4) * EPL;               // block offset inside the step
     const uint8_t* ep = exp + row * nbk + kb0 / 16 + b0;
-    if (full && a.exp_vec) {
+    if (WHOLE || (full && a.exp_vec)) {
       if constexpr (EPL == 2) r.e[0] = *reinterpret_cast<const uint16_t*>(ep);
       else if constexpr (EPL == 4) r.e[0] = *reinterpret_cast<const uint32_t*>(ep);
       else {
@@ -233,54 +233,6 @@ __device__ __forceinline__ void load_step(StepRegs<FMT, G>& r, const uint8_t* co
         if (kb0 + 16 * (b0 + b) < a.k) r.e[b / 4] |= (uint32_t)ep[b] << (8 * (b % 4));
     }
   }
-}
-
-// Exponents of four steps in one load (every step whole, the exponent array aligned to a step's
-// 8G exponent bytes): lane 4 r + q takes all 8G exponent bytes of row r in step min(s0 + q,
-// slast). A row's exponents for consecutive steps are contiguous, so the 16 rows cost one load
-// of 32G bytes each instead of four of 8G.
-template <int G>
-__device__ __forceinline__ void load_exp4(uint32_t (&v)[2 * G], const uint8_t* exp, int row0, const MgArgs& a,
-                                          int s0, int slast, int lane) {
-  static_assert(G == 1 || G == 2, "one or two 128-value units per step");
-  const int nbk = a.k / kBlock;
-  const int64_t row = min(row0 + lane / 4, a.n - 1);
-  const int st = min(s0 + lane % 4, slast);
-  const uint8_t* ep = exp + row * nbk + st * 8 * G;
-  if constexpr (G == 1) {
-    const u32x2 x = *reinterpret_cast<const u32x2*>(ep);
-    v[0] = x.x; v[1] = x.y;
-  } else {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(ep);
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-  }
-}
-
-// One stage of a 4 x 4 transpose inside each quad of lanes: where bit B of the lane (in its quad)
-// and of the slot differ, the slot takes the partner lane's (lane ^ B) slot ^ B.
-template <int B>
-__device__ __forceinline__ void quad_xchg(uint32_t (&o)[4], int q) {
-  constexpr int ctrl = B == 1 ? 0xb1 : 0x4e;     // DPP quad_perm [1,0,3,2] / [2,3,0,1]
-#pragma unroll
-  for (int s0 = 0; s0 < 4; ++s0) {
-    if (s0 & B) continue;
-    const int s1 = s0 | B;
-    const uint32_t t0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o[s0], ctrl, 0xf, 0xf, false);
-    const uint32_t t1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o[s1], ctrl, 0xf, 0xf, false);
-    if (q & B) o[s0] = t1;
-    else o[s1] = t0;
-  }
-}
-
-// From load_exp4's registers to the per-step lane order of StepRegs: lane 4 r + q holds the four
-// 2G-byte slots of step s0 + q; afterwards its slot p is slot q of step s0 + p, the bytes a
-// per-step load gives lane 4 r + q in step s0 + p (one slot per dword, low bytes).
-template <int G>
-__device__ __forceinline__ void exp4_transpose(uint32_t (&o)[4], const uint32_t (&v)[2 * G], int lane) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) o[s] = G == 2 ? v[s] : (v[s / 2] >> (16 * (s % 2))) & 0xffffu;
-  quad_xchg<1>(o, lane & 3);
-  quad_xchg<2>(o, lane & 3);
 }
 
 // ---- the kernel ---------------------------------------------------------------------------
@@ -305,16 +257,16 @@ struct WaveLds {
   static constexpr int kRS = R::kRB + 16;
   static constexpr int kES = R::kEB + (G == 4 ? 8 : 4);
   static constexpr int kBytes = 16 * kRS + 16 * kES;
-  // row-contiguous, as loaded (ev: the lane's exponent bytes, StepRegs::e or a group's slot)
-  static __device__ __forceinline__ void put(uint8_t* w, const R& r, const uint32_t* ev, int lane) {
+  // row-contiguous, as loaded
+  static __device__ __forceinline__ void put(uint8_t* w, const R& r, int lane) {
     constexpr int CPR = R::kRB / 16, RPL = 64 / CPR, EPL = R::kEB / 4;
 #pragma unroll
     for (int q = 0; q < R::kLoads; ++q)
       *reinterpret_cast<u32x4*>(w + (q * RPL + lane / CPR) * kRS + (lane % CPR) * 16) = r.c[q];
     uint8_t* e = w + 16 * kRS + (lane / 4) * kES + (lane % 4) * EPL;
-    if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(e) = (uint16_t)ev[0];
-    else if constexpr (EPL == 4) *reinterpret_cast<uint32_t*>(e) = ev[0];
-    else *reinterpret_cast<u32x2*>(e) = u32x2{ev[0], ev[1]};
+    if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(e) = (uint16_t)r.e[0];
+    else if constexpr (EPL == 4) *reinterpret_cast<uint32_t*>(e) = r.e[0];
+    else *reinterpret_cast<u32x2*>(e) = u32x2{r.e[0], r.e[1]};
   }
   // MFMA operand order: row c, values [g LV, (g + 1) LV) and their 2G exponents
   static __device__ __forceinline__ void get(const uint8_t* w, uint32_t* cw, uint32_t* ew, int c, int g) {
@@ -371,39 +323,18 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_gemv_kernel(MgArgs a) {
 
   constexpr int D = NMAT == 1 ? 2 : 1;            // prefetch distance in steps
   R ra[NMAT], rb[NMAT], rc[NMAT];
-  // grouped exponents (exp_grp): groups of four steps from the slice start; gn holds the next
-  // group as loaded (issued with the codes of its first step), ge the current one transposed,
-  // slot 0 the step being computed
-  uint32_t gn[NMAT][2 * G], ge[NMAT][4];
-  auto load = [&](R (&r)[NMAT], int st, auto grp) __attribute__((always_inline)) {
-    constexpr bool GRP = decltype(grp)::value;
+  auto load = [&](R (&r)[NMAT], int st, auto whole) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < NMAT; ++t) load_step<FMT, G, !GRP>(r[t], a.code[t], a.exp[t], col0, a, st, lane);
-    if constexpr (GRP) {
-      if ((st - st0) % 4 == 0)
-#pragma unroll
-        for (int t = 0; t < NMAT; ++t) load_exp4<G>(gn[t], a.exp[t], col0, a, st, st1 - 1, lane);
-    }
+    for (int t = 0; t < NMAT; ++t)
+      load_step<FMT, G, decltype(whole)::value>(r[t], a.code[t], a.exp[t], col0, a, st, lane);
   };
-  auto compute = [&](R (&r)[NMAT], int st, int kb, auto grp) __attribute__((always_inline)) {
-    constexpr bool GRP = decltype(grp)::value;
-    if constexpr (GRP) {
-      if ((st - st0) % 4 == 0)
-#pragma unroll
-        for (int t = 0; t < NMAT; ++t) exp4_transpose<G>(ge[t], gn[t], lane);
-    }
+  auto compute = [&](R (&r)[NMAT], int st, int kb) __attribute__((always_inline)) {
     // through this wave's LDS area: row-contiguous as loaded, read back as MFMA operands
     // (lane l: weight row l % 16, values [(l / 16) LV, +LV) of the step)
     uint32_t cw[NMAT][LaneCodes<FMT, G>::kDw];
     uint32_t ew[NMAT][(2 * G + 3) / 4];
 #pragma unroll
-    for (int t = 0; t < NMAT; ++t) W::put(wl + t * W::kBytes, r[t], GRP ? ge[t] : r[t].e, lane);
-    if constexpr (GRP) {
-#pragma unroll
-      for (int t = 0; t < NMAT; ++t) {
-        ge[t][0] = ge[t][1]; ge[t][1] = ge[t][2]; ge[t][2] = ge[t][3];
-      }
-    }
+    for (int t = 0; t < NMAT; ++t) W::put(wl + t * W::kBytes, r[t], lane);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int t = 0; t < NMAT; ++t) W::get(wl + t * W::kBytes, cw[t], ew[t], c, g);
@@ -460,34 +391,58 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_gemv_kernel(MgArgs a) {
   };
 
   // the first weights are in flight while the activations are staged; loads run D steps
-  // ahead of the MFMAs (register sets used in rotation)
-  auto run = [&](auto grp) __attribute__((always_inline)) {
-    auto body = [&](R (&cur)[NMAT], R (&nxt)[NMAT], int st) __attribute__((always_inline)) {
-      const int kb = chunk_at(st);
-      if (st + D < st1) load(nxt, st + D, grp);
-      compute(cur, st, kb, grp);
-    };
-    load(ra, st0, grp);
+  // ahead of the MFMAs (register sets used in rotation). The steady loop issues every load
+  // unconditionally, in one form (whole steps): a load behind a branch, or a step whose loads
+  // may take another form, leaves the compiler unable to count the loads in flight, and it
+  // then waits for all of them (the prefetch included) before each step. The last steps take
+  // the guarded form.
+  auto body = [&](R (&cur)[NMAT], R (&nxt)[NMAT], int st, auto whole) __attribute__((always_inline)) {
+    const int kb = chunk_at(st);
+    if (st + D < st1) load(nxt, st + D, whole);
+    compute(cur, st, kb);
+  };
+  auto body_steady = [&](R (&cur)[NMAT], R (&nxt)[NMAT], int st) __attribute__((always_inline)) {
+    const int kb = chunk_at(st);
+    load(nxt, st + D, Flag<true>{});
+    compute(cur, st, kb);
+  };
+  auto run = [&](auto whole) __attribute__((always_inline)) {
+    constexpr bool WH = decltype(whole)::value;
+    int st = st0;
+    load(ra, st0, whole);
     if constexpr (D == 1) {
-      for (int st = st0; st < st1; st += 2) {
-        body(ra, rb, st);
-        if (st + 1 < st1) body(rb, ra, st + 1);
+      if constexpr (WH) {
+        for (; st + 2 < st1; st += 2) {
+          body_steady(ra, rb, st);
+          body_steady(rb, ra, st + 1);
+        }
+      }
+      for (; st < st1; st += 2) {
+        body(ra, rb, st, whole);
+        if (st + 1 < st1) body(rb, ra, st + 1, whole);
       }
     } else {
-      if (st0 + 1 < st1) load(rb, st0 + 1, grp);
-      for (int st = st0; st < st1; st += 3) {
-        body(ra, rc, st);
-        if (st + 1 < st1) body(rb, ra, st + 1);
-        if (st + 2 < st1) body(rc, rb, st + 2);
+      if (WH && st0 + 4 < st1) {
+        load(rb, st0 + 1, whole);   // unconditional: the loop starts with exactly two steps in flight
+        for (; st + 4 < st1; st += 3) {
+          body_steady(ra, rc, st);
+          body_steady(rb, ra, st + 1);
+          body_steady(rc, rb, st + 2);
+        }
+      } else if (st0 + 1 < st1) {
+        load(rb, st0 + 1, whole);
+      }
+      for (; st < st1; st += 3) {
+        body(ra, rc, st, whole);
+        if (st + 1 < st1) body(rb, ra, st + 1, whole);
+        if (st + 2 < st1) body(rc, rb, st + 2, whole);
       }
     }
   };
-  if constexpr (G <= 2 && MT == 1) {   // (two tiles: the group registers would cost occupancy)
-    if (a.exp_grp) run(Flag<true>{});
-    else run(Flag<false>{});
-  } else {
-    run(Flag<false>{});
-  }
+  // (slices too short for one pass of the steady loop keep the guarded form throughout: it was
+  // faster there, 2-step slices of the QKV / O projections at m = 16)
+  if (a.whole && st1 - st0 >= 2 * D + 1) run(Flag<true>{});
+  else run(Flag<false>{});
 
   // element i of a 16x16 output tile: activation row 4 g + i, column c
   auto store = [&](int yr, int yc, const float* v) __attribute__((always_inline)) {
@@ -640,7 +595,7 @@ hipError_t launch_mt(MgArgs a, hipStream_t s) {
   const int nbk = a.k / kBlock;
   const uintptr_t ep = reinterpret_cast<uintptr_t>(a.exp[0]) | reinterpret_cast<uintptr_t>(a.exp[1]);
   a.exp_vec = (nbk % (2 * G)) == 0 && (ep % (2 * G)) == 0;
-  a.exp_grp = G <= 2 && a.k % SK == 0 && ep % (8 * G) == 0;
+  a.whole = a.k % SK == 0 && (FMT == 8 || a.code16) && a.exp_vec;
   // activations: the whole slice if it fits, else chunks of whole steps
   const size_t per_k = (size_t)XS * a.m * sizeof(uint16_t);
   const int slice_k = a.sps * SK;
