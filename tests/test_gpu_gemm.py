@@ -168,6 +168,50 @@ def test_gemm_rows_independent_of_m_long_k(x_dtype):
     assert_within(y32, oracle.gemm(x64, wd), oracle.normaliser(x64, wd), TOL, what="gemm long K")
 
 
+def _sampled_rows_from_device(wm, idx):
+    """The oracle's fp64 values of weight rows idx of a device BfpMatrix (read back, decoded)."""
+    nb = wm.k // 16
+    cpr = wm.code.numel() // wm.n
+    e = wm.exp.view(wm.n, nb)[idx].cpu().numpy()
+    c = wm.code.view(wm.n, cpr)[idx].cpu().numpy()
+    return oracle.decode(e, c, wm.fmt, len(idx), wm.k)
+
+
+@pytest.mark.parametrize("fmt", [BFP8, BFP4])
+@pytest.mark.parametrize("steps", [3, 9, 13])
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("m", [8, 32])
+def test_gemm_long_slices(fmt, steps, swiglu, m):
+    """25,600 weight rows, so that K is cut into few, long slices: with 3 / 9 / 13 steps of K
+    the slices hold 3 / 5 + 4 / 7 + 6 steps, around the lengths at which the matrix-core kernel
+    switches between its steady loop (every load unconditional) and its guarded form, for one
+    and two matrices and one and two row tiles. Weights quantized on the device (bit-exact with
+    the oracle's encoding, tested elsewhere); 160 sampled output columns (the first and last
+    rows of the matrix among them) against the oracle on the read-back blocks."""
+    n = 25600
+    sk = 128 if fmt == BFP8 else 256
+    k = steps * sk
+    note(f"gemm long slices fmt={fmt} k={k} swiglu={swiglu} m={m}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 * steps + 10 * fmt + m + int(swiglu))
+    wm = bfq.bfp_quantize(fmt, torch.randn((n, k), generator=gen, device="cuda") * 0.02)
+    um = bfq.bfp_quantize(fmt, torch.randn((n, k), generator=gen, device="cuda") * 0.02) if swiglu else None
+    rng = np.random.default_rng(steps + m)
+    xb = synth.bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    x64 = oracle.bf16_to_f64(xb)
+    y = bfq.bfp_gemm(wm, dev_bf16(xb), w_up=um).cpu().numpy()
+    idx = np.unique(np.concatenate([[0, 127, 128, n - 1], rng.choice(n, 156, replace=False)]))
+    wd = _sampled_rows_from_device(wm, idx)
+    if swiglu:
+        ud = _sampled_rows_from_device(um, idx)
+        g, u = oracle.gemm(x64, wd), oracle.gemm(x64, ud)
+        ref = oracle.swiglu(g, u)
+        norm = 1.1 * oracle.normaliser(x64, wd) * np.abs(u) + np.abs(oracle.silu(g)) * oracle.normaliser(x64, ud)
+        assert_within(y[:, idx], ref, norm, TOL, extra=1e-6 * np.abs(ref), what="long slices swiglu")
+    else:
+        assert_within(y[:, idx], oracle.gemm(x64, wd), oracle.normaliser(x64, wd), TOL, what="long slices")
+
+
 @pytest.mark.parametrize("fmt", [BFP8, BFP4])
 @pytest.mark.parametrize("n,k,x_dtype,swiglu", [(300, 2064, "bf16", False), (96, 17408, "bf16", True),
                                                  (200, 1040, "f32", False), (5000, 2048, "bf16", False)])
